@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for the Muon step.  Test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package; the HIP library never does.
+"""
+from .muon_oracle import (  # noqa: F401
+    DEFAULT_LR, DEFAULT_MOMENTUM, DEFAULT_NS_STEPS, DEFAULT_WEIGHT_DECAY,
+    NS_COEFFICIENTS, NS_EPS, RMS_MATCH, VARIANT_MUON, VARIANT_MUONGS,
+    frobenius_inner, muon_step, muongs_project, nesterov_momentum,
+    newton_schulz, update_scale,
+)

@@ -1,0 +1,187 @@
+"""Muon / MuonGS optimizer step: plain fp64 NumPy oracle.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+helper with the HIP library and imports nothing from it.
+
+It is deliberately slow and literal: every step is written in the order and
+notation of the pages it follows, in float64, with NumPy's ``@`` as the only
+library primitive (no symmetric tricks, no blocking, no fusion).
+
+Citation keys (the pages this follows; a section, code block or equation is
+named after the key):
+
+  [LS] "LLM Pretraining Loss Spike 진단과 처방: 배치 사이즈, Gradient
+       Accumulation, 그리고 Muon 전환 판단" (juhoplayground.github.io), section
+       "AdamW에서 Muon으로 갈아탈 것인가".
+  [GS] "MuonGS: Pretraining LLMs with Relaxed Weight-Norm Control"
+       (onedev.kr paper summary).
+  [MS] "[논문 AI 리뷰] MUON IS SCALABLE FOR LLM TRAINING TECHNICAL REPORT"
+       (blog.pieroot.xyz), section "2. Key Methods and Approach".
+  [MX] "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저"
+       (codersblog.github.io).
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes of the repository):
+
+  * Momentum is the SGD form M' = mu*M + G ("before Newton-Schulz, Muon is
+    just SGD-momentum", [LS]); Nesterov look-ahead U = G + mu*M' (the pages
+    name Nesterov as the default but print no formula).
+  * The Newton-Schulz iteration runs on the shorter side: a tall matrix
+    (rows > cols) is transposed first and the result transposed back ([MX]
+    section 2: a rectangular update becomes semi-orthogonal).
+  * Update scale is Moonlight's 0.2*sqrt(max(A, B)) ([MS] eq. 4); weight decay
+    is decoupled and uses the unscaled learning rate ([LS] Moonlight section,
+    "AdamW식 weight decay"; [MX] section 3 step 5).
+  * MuonGS projects O against the pre-decay W; if ||W||_F == 0 the projection
+    is the identity.  Weight decay, when non-zero, is applied in every variant.
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests
+(closed forms, invariants, library special cases); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# [LS] section "Muon head의 실체는 하이브리드 옵티마이저다", the Newton-Schulz
+# code block: the quintic coefficients as printed (a, b, c).
+NS_COEFFICIENTS = (3.4445, -4.7750, 2.0315)
+# Same code block: the stabiliser added to the Frobenius norm.
+NS_EPS = 1e-7
+# [LS] same section, the listed defaults: lr 0.02, momentum 0.95 (Nesterov),
+# ns_steps 5.  Weight decay 0.1 is [MX] section 5's example.
+DEFAULT_LR = 0.02
+DEFAULT_MOMENTUM = 0.95
+DEFAULT_NS_STEPS = 5
+DEFAULT_WEIGHT_DECAY = 0.1
+# [MS] eq. 4 (and [LS] Moonlight section): the constant that matches AdamW's
+# update RMS.
+RMS_MATCH = 0.2
+
+VARIANT_MUON = "muon"
+VARIANT_MUONGS = "muongs"
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def frobenius_inner(X, Y) -> float:
+    """<X, Y>_F = sum_ij X_ij Y_ij  ([GS] "전제와 한계": the <W_t, O_t>_F term)."""
+    return float(np.sum(_f64(X) * _f64(Y)))
+
+
+def nesterov_momentum(G, M, momentum):
+    """Momentum accumulation, then the Nesterov look-ahead.
+
+    [MX] section 3, step 2 (accumulate the previous state with the current
+    gradient; Nesterov by default) and [LS] "Muon head" section (SGD-momentum,
+    momentum 0.95, nesterov True):
+
+        M' = mu * M + G          (SGD-momentum buffer)
+        U  = G + mu * M'         (Nesterov look-ahead; the matrix handed to NS)
+
+    Returns (M', U).
+    """
+    G = _f64(G)
+    M = _f64(M)
+    M_new = momentum * M + G
+    U = G + momentum * M_new
+    return M_new, U
+
+
+def newton_schulz(U, a, b, c, steps, eps=NS_EPS):
+    """Approximate the orthogonal polar factor (U U^T)^{-1/2} U.
+
+    [LS] Newton-Schulz code block and [MS] section 2: starting from
+    X_0 = U / (||U||_F + eps), repeat ``steps`` times
+
+        A = X X^T
+        B = b*A + c*A A
+        X = a*X + B X
+
+    which is X_k = a X + b (X X^T) X + c (X X^T)^2 X.  The iteration runs on
+    the shorter side ([MX] section 2): a tall U (rows > cols) is transposed
+    before and after.  ``steps == 0`` returns the normalised X_0.
+    """
+    U = _f64(U)
+    if U.ndim != 2:
+        raise ValueError("Newton-Schulz needs a 2-D matrix")
+    transposed = U.shape[0] > U.shape[1]
+    X = U.T if transposed else U
+    X = X / (np.linalg.norm(X, "fro") + eps)
+    for _ in range(steps):
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X.T if transposed else X
+
+
+def muongs_project(W, O):
+    """Gram-Schmidt radial projection of the update ([GS] "전제와 한계"):
+
+        O~ = O - (<W, O>_F / r^2) W,   r = ||W||_F.
+
+    With r == 0 there is no radial direction and O is returned unchanged.
+    """
+    W = _f64(W)
+    O = _f64(O)
+    r2 = frobenius_inner(W, W)
+    if r2 == 0.0:
+        return O.copy()
+    return O - (frobenius_inner(W, O) / r2) * W
+
+
+def update_scale(rows, cols):
+    """Moonlight RMS matching, [MS] eq. 4: the factor 0.2 * sqrt(max(A, B))."""
+    return RMS_MATCH * float(np.sqrt(max(rows, cols)))
+
+
+def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
+              weight_decay=DEFAULT_WEIGHT_DECAY, ns_steps=DEFAULT_NS_STEPS,
+              a=NS_COEFFICIENTS[0], b=NS_COEFFICIENTS[1], c=NS_COEFFICIENTS[2],
+              variant=VARIANT_MUON, eps=NS_EPS):
+    """One Muon (or MuonGS) step on one 2-D hidden weight, in fp64.
+
+    The order is [MX] section 3: momentum (Nesterov), magnitude normalisation,
+    Newton-Schulz, then the shape scale and decoupled weight decay, then the
+    parameter update.  MuonGS ([GS]) replaces O by its projection O~ before
+    the update.
+
+        M'  = mu M + G;  U = G + mu M'
+        O   = NS_{a,b,c}^{ns_steps}(U)
+        O~  = O - (<W,O>/||W||^2) W        (MuonGS only)
+        s   = 0.2 sqrt(max(A, B))
+        W'  = (1 - lr*wd) W - lr * s * O~
+
+    Returns (W', M', stats) where stats holds the scalars the library can
+    report: norm_U = ||U||_F, r2 = ||W||_F^2, dot_WO = <W,O>_F,
+    norm2_O = ||O||_F^2 and norm2_Ot = ||O~||_F^2 (O~ = O for plain Muon).
+    """
+    W = _f64(W)
+    G = _f64(G)
+    M = _f64(M)
+    if W.ndim != 2:
+        # [MX] section 5: a non-2-D parameter is an error for Muon.
+        raise ValueError("Muon updates 2-D weight matrices only")
+    if G.shape != W.shape or M.shape != W.shape:
+        raise ValueError("W, G and M must have the same shape")
+    if variant not in (VARIANT_MUON, VARIANT_MUONGS):
+        raise ValueError(f"unknown variant {variant!r}")
+    rows, cols = W.shape
+
+    M_new, U = nesterov_momentum(G, M, momentum)
+    O = newton_schulz(U, a, b, c, ns_steps, eps)
+    O_t = muongs_project(W, O) if variant == VARIANT_MUONGS else O
+    s = update_scale(rows, cols)
+    W_new = (1.0 - lr * weight_decay) * W - lr * s * O_t
+
+    stats = {
+        "norm_U": float(np.linalg.norm(U, "fro")),
+        "r2": frobenius_inner(W, W),
+        "dot_WO": frobenius_inner(W, O),
+        "norm2_O": frobenius_inner(O, O),
+        "norm2_Ot": frobenius_inner(O_t, O_t),
+    }
+    return W_new, M_new, stats

@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Muon optimizer step benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt160m]
+
+A step is one whole Muon step over every hidden 2-D matrix of the workload:
+momentum/Nesterov head, 5 Newton-Schulz iterations, scale/decay/update tail,
+issued as ONE grouped launch sequence (muon_step_grouped) on inputs already
+resident in HBM.  Prints one JSON line:
+
+  value       optimizer steps per second (whole job = one GPU)
+  roofline    the dominant kernel (the Newton-Schulz update GEMM): its
+              algorithmic flops per launch over its average launch time,
+              timed live with HIP events on the launch stream
+  ns / head / tail   phase figures: NS TFLOP/s vs the bf16 MFMA peak and the
+              elementwise phases' GB/s vs HBM peak
+  cpu_baseline  the fp64 oracle on the host cores on a bounded sample of the
+              same matrices, extrapolated to the full workload
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "Muon optimizer steps/sec (full model) + NS TFLOP/s as % of bf16 MFMA peak"
+PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}   # dense, published MI355X figures
+PEAK_HBM = 8.0e12
+HP = dict(lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5)
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt160m")
+    ap.add_argument("--variant", default="muon", choices=["muon", "muongs"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phase-profile", action="store_true")
+    return ap.parse_args()
+
+
+def matrix_work(groups, dtype_bytes):
+    """Algorithmic work per step, from the true (unpadded) shapes."""
+    gram = poly = upd = 0.0
+    elems = 0
+    for g in groups:
+        p, q = min(g.rows, g.cols), max(g.rows, g.cols)
+        gram += g.count * p * p * q            # symmetric X X^T: half of 2p^2q
+        poly += g.count * p ** 3               # symmetric A A^T: half of 2p^3
+        upd += g.count * 2.0 * p * p * q       # B X
+        elems += g.count * g.rows * g.cols
+    es = dtype_bytes
+    return dict(gram=gram, poly=poly, update=upd, elems=elems,
+                head_bytes=elems * (es + 4 + 4 + es),   # G r, M r+w, X0 w
+                tail_bytes=elems * (es + es + es))      # W r, O r, W w
+
+
+def cpu_baseline(wl_mod, w, seconds):
+    """The oracle, untuned, on whole matrices drawn in layer order until about
+    `seconds` of CPU time, extrapolated to the full matrix count."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()
+                       if t.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    per_shape = {}
+    order = []
+    # one matrix of each group per "layer", round-robin; values are seeded
+    # Gaussians of the workload's distributions (the oracle's cost depends on
+    # the shapes only)
+    for k in range(max(g.count for g in w.groups)):
+        for gi, g in enumerate(w.groups):
+            if k < g.count:
+                order.append((gi, k))
+    spent = 0.0
+    done = 0
+    for gi, k in order:
+        g = w.groups[gi]
+        gen = torch.Generator().manual_seed(10_000 + 131 * gi + k)
+        W = (torch.randn(g.rows, g.cols, generator=gen) * 0.02).to(wl_mod.torch_dtype(w.dtype))
+        G = (torch.randn(g.rows, g.cols, generator=gen) * 1e-3).to(wl_mod.torch_dtype(w.dtype))
+        Wd = W.double().numpy()
+        Gd = G.double().numpy()
+        Md = np.zeros_like(Wd)
+        t0 = time.perf_counter()
+        oracle.muon_step(Wd, Gd, Md, **HP)
+        dt = time.perf_counter() - t0
+        per_shape.setdefault((g.rows, g.cols), []).append(dt)
+        spent += dt
+        done += 1
+        if spent >= seconds and len(per_shape) == len(w.groups):
+            break
+    total = sum(g.count * (sum(per_shape[(g.rows, g.cols)]) / len(per_shape[(g.rows, g.cols)]))
+                for g in w.groups)
+    return {"value": 1.0 / total, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.n_matrices} matrices (round-robin over the shape groups), "
+                      f"{spent:.1f} s of fp64 NumPy; seconds/step extrapolated per shape",
+            "seconds_per_step": total, "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): this build has no multi-GPU path; each GPU would run the same "
+              "step on its own share of the matrices.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from muon_step_03_amd import _lib, muon_step_grouped, stacked_group, workspace_bytes_grouped
+    from muon_step_03_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    tdtype = wl.torch_dtype(w.dtype)
+    es = 2 if w.dtype == wl.BF16 else 4
+
+    Ws = wl.make_weights(w, dev)
+    Gs = wl.make_grads(w, 0, dev)
+    Ms = wl.make_momentum(w, dev)
+    groups = [stacked_group(Ws[i], Gs[i], Ms[i]) for i in range(len(w.groups))]
+    ws = torch.empty(workspace_bytes_grouped(groups, tdtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    hp = dict(HP, ns_coefficients=NS_COEFFS, variant=args.variant)
+
+    def step():
+        muon_step_grouped(groups, tdtype, workspace=ws, device=dev, stream=stream, **hp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # ---- timed region: exactly K steps, synchronised on both sides
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ev_ms = start.elapsed_time(stop)
+    ms_per_step = max(ev_ms, wall_ms) / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    work = matrix_work(w.groups, es)
+    result = {
+        "metric": METRIC, "value": 1e3 / ms_per_step, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian W ~ N(0, 0.02^2), G ~ N(0, 1e-3^2), M = 0)",
+        "config": {"workload": w.name, "description": w.description, "matrices": w.n_matrices,
+                   "elements": w.n_elements, "variant": args.variant, "ns_steps": 5,
+                   "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1,
+                   "launch": "muon_step_grouped (one launch sequence per step)"},
+    }
+
+    # ---- per-launch kernel times with HIP events on the launch stream
+    if not args.no_phase_profile:
+        L = _lib.lib()
+        L.muon_profile_enable(1)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        L.muon_profile_enable(0)
+        n = _lib.MUON_NUM_PHASES
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        assert L.muon_profile_read(ms, cnt, n) == 0
+        avg = {L.muon_phase_name(i).decode(): (ms[i] / cnt[i] if cnt[i] else 0.0) for i in range(n)}
+        per_step = {L.muon_phase_name(i).decode(): ms[i] / args.steps for i in range(n)}
+        peak = PEAK_MFMA[w.dtype]
+        upd_flops = work["update"]
+        a = upd_flops / (avg["update"] * 1e-3)
+        result["roofline"] = {
+            "kernel": "ns_update (X' = aX + B X)", "bound": "mfma",
+            "achieved": a / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s", "frac": a / peak,
+            "traffic": None, "avg_launch_ms": avg["update"],
+            "alg_flops_per_launch": upd_flops,
+        }
+        ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"]
+        ns_flops = 5 * (work["gram"] + work["poly"] + work["update"])
+        result["ns"] = {"ms_per_step": ns_ms, "tflops": ns_flops / (ns_ms * 1e-3) / 1e12,
+                        "frac_of_peak": ns_flops / (ns_ms * 1e-3) / peak,
+                        "alg_tflop_per_step": ns_flops / 1e12,
+                        "avg_launch_ms": {k: avg[k] for k in ("gram", "poly", "update")}}
+        result["head"] = {"ms": avg["head"], "gbps": work["head_bytes"] / (avg["head"] * 1e-3) / 1e9,
+                          "frac_of_hbm": work["head_bytes"] / (avg["head"] * 1e-3) / PEAK_HBM}
+        tail_ms = per_step["tail_apply"] + per_step["tail_reduce"] + per_step["tail_finalize"]
+        result["tail"] = {"ms": tail_ms, "gbps": work["tail_bytes"] / (tail_ms * 1e-3) / 1e9,
+                          "frac_of_hbm": work["tail_bytes"] / (tail_ms * 1e-3) / PEAK_HBM}
+        result["phase_ms_per_step"] = per_step
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

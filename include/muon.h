@@ -1,0 +1,171 @@
+/*
+ * muon.h — C ABI of the MI355X (gfx950) Muon optimizer step.
+ *
+ * One call performs one optimizer step on 2-D hidden-layer weight matrices:
+ *
+ *   M' = mu*M + G;  U = G + mu*M'                 momentum, Nesterov look-ahead
+ *   X0 = U / (||U||_F + 1e-7)                     (U^T first if rows > cols)
+ *   repeat ns_steps:  A = X X^T;  B = b*A + c*A*A;  X = a*X + B*X
+ *   O  = X (transposed back if rows > cols)
+ *   O~ = O - (<W,O>_F / ||W||_F^2) W              MuonGS only, when ||W|| > 0
+ *   W' = (1 - lr*wd) W - lr * 0.2*sqrt(max(rows,cols)) * O~
+ *
+ * Sources (page title and passage):
+ *  - update order: "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저"
+ *    (codersblog.github.io), section 3 "Muon의 업데이트 순서", steps 1-5;
+ *  - momentum 0.95 / Nesterov / 5 steps / coefficients (3.4445, -4.7750, 2.0315)
+ *    / 1e-7: "LLM Pretraining Loss Spike 진단과 처방 ... Muon 전환 판단"
+ *    (juhoplayground.github.io), section "Muon head의 실체는 하이브리드
+ *    옵티마이저다", Newton-Schulz code block and the defaults after it;
+ *  - the iteration X_k = aX + b(XX^T)X + c(XX^T)^2 X approximating
+ *    (MM^T)^{-1/2}M and the 0.2*sqrt(max(A,B)) scale (eq. 4): "[논문 AI 리뷰]
+ *    MUON IS SCALABLE FOR LLM TRAINING TECHNICAL REPORT" (blog.pieroot.xyz),
+ *    section 2 "Key Methods and Approach";
+ *  - decoupled (AdamW-style) weight decay: the loss-spike page, section
+ *    "Moonlight와 MuonClip이 추가한 것";
+ *  - MuonGS projection: "MuonGS: Pretraining LLMs with Relaxed Weight-Norm
+ *    Control" (onedev.kr), the Gram-Schmidt update in "전제와 한계";
+ *  - non-2-D parameters are errors: the codersblog page, section 5.
+ *
+ * Momentum is the SGD form (M' = mu*M + G), the plainest reading of the
+ * pages' "SGD-momentum"; Nesterov is always on (the pages' default).
+ * Weight decay uses the unscaled learning rate and applies in every variant.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Memory   W, G and M are DEVICE pointers to row-major rows x cols matrices.
+ *           W and G hold `dtype` elements, M is always float32.  G is read
+ *           only; W and M are updated in place.  W, G, M and the workspace
+ *           must not overlap.  The caller owns every buffer.
+ *  Dtype    MUON_DTYPE_F32: W, G float32; the iteration runs in float32.
+ *           MUON_DTYPE_BF16: W, G bfloat16; the iteration runs on bf16
+ *           matrix cores with float32 accumulation and float32 epilogues;
+ *           W' is rounded to bfloat16 (round to nearest even).
+ *  Workspace  device memory of at least the size the matching
+ *           muon_workspace_bytes* call returns; any alignment; its contents
+ *           on entry are ignored and are garbage on exit.
+ *  Stats    optional device float array, MUON_STATS_PER_MATRIX floats per
+ *           matrix (matrix order: group by group, then index within the
+ *           group): ||U||_F, ||W||_F^2, <W,O>_F, ||O||_F^2, ||O~||_F^2, all
+ *           computed in float32 on the GPU.  NULL skips them.
+ *  Stream   a hipStream_t passed as void*; NULL is the default stream.  The
+ *           call only enqueues work: it does not synchronise, allocate device
+ *           memory or copy to the host.  Kernel faults surface at the
+ *           caller's next synchronisation on that stream.
+ *  Errors   every entry point returns a muon_status.  All arguments are
+ *           validated before any work is enqueued; on an error nothing is
+ *           enqueued and W, M are untouched.  MUON_ERR_HIP means a launch
+ *           failed; earlier launches of the same call may have run.
+ *           muon_status_string() names a status.
+ *  Hyperparameters  lr, momentum, weight_decay, a, b, c must be finite;
+ *           ns_steps in [0, MUON_MAX_NS_STEPS]; ns_steps == 0 is legal and
+ *           gives O = X0.  variant is MUON_VARIANT_MUON or _MUONGS.
+ *  Shapes   1 <= rows, cols <= MUON_MAX_DIM.  An empty batch (count == 0 or
+ *           ngroups == 0) is a no-op returning MUON_OK.
+ *  Concurrency  calls on different streams must use different workspaces.
+ */
+#ifndef MUON_MI355X_MUON_H
+#define MUON_MI355X_MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad count, non-finite or out-of-range scalar */
+  MUON_ERR_INVALID_SHAPE = 2,     /* rows or cols outside [1, MUON_MAX_DIM] */
+  MUON_ERR_UNSUPPORTED_DTYPE = 3, /* dtype not MUON_DTYPE_F32 / MUON_DTYPE_BF16 */
+  MUON_ERR_WORKSPACE_TOO_SMALL = 4,
+  MUON_ERR_HIP = 5                /* a HIP runtime call or kernel launch failed */
+} muon_status;
+
+enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 };
+enum { MUON_VARIANT_MUON = 0, MUON_VARIANT_MUONGS = 1 };
+
+#define MUON_STATS_PER_MATRIX 5
+#define MUON_MAX_DIM 32768
+#define MUON_MAX_NS_STEPS 100
+/* Groups handled by one launch sequence of muon_step_grouped; more groups are
+ * processed as further sequences on the same stream. */
+#define MUON_GROUPS_PER_LAUNCH 8
+
+/*
+ * A group: `count` matrices of one shape rows x cols.  Give EITHER device
+ * pointer tables (W_table, G_table, M_table: device arrays of `count` device
+ * pointers each, entries not checked on the host) OR contiguous stacks
+ * (W, G, M: device pointers to [count][rows][cols] arrays).  The three
+ * pointers of the unused form must be NULL.
+ */
+typedef struct muon_group {
+  int64_t count;
+  int64_t rows;
+  int64_t cols;
+  void* const* W_table;
+  const void* const* G_table;
+  float* const* M_table;
+  void* W;
+  const void* G;
+  float* M;
+} muon_group;
+
+/* Workspace bytes for muon_step / muon_step_batched on count matrices of
+ * rows x cols (0 on invalid arguments). */
+size_t muon_workspace_bytes(int64_t count, int64_t rows, int64_t cols, int dtype);
+
+/* Workspace bytes for muon_step_grouped over these groups (0 on invalid
+ * arguments). */
+size_t muon_workspace_bytes_grouped(const muon_group* groups, int ngroups, int dtype);
+
+/* One step on one matrix.  W, G, M: device pointers (see conventions). */
+int muon_step(void* W, const void* G, float* M, int64_t rows, int64_t cols, int dtype,
+              double lr, double momentum, double weight_decay, int ns_steps,
+              double a, double b, double c, int variant,
+              void* workspace, size_t workspace_bytes, float* stats, void* stream);
+
+/* One step on `count` same-shape matrices (per-layer stacks, MoE experts).
+ * W, G, M: device arrays of `count` device pointers. */
+int muon_step_batched(void* const* W, const void* const* G, float* const* M, int64_t count,
+                      int64_t rows, int64_t cols, int dtype,
+                      double lr, double momentum, double weight_decay, int ns_steps,
+                      double a, double b, double c, int variant,
+                      void* workspace, size_t workspace_bytes, float* stats, void* stream);
+
+/* One step on several shape groups at once (a whole model): every phase is
+ * one launch over the work of all groups.  `groups` is a HOST array. */
+int muon_step_grouped(const muon_group* groups, int ngroups, int dtype,
+                      double lr, double momentum, double weight_decay, int ns_steps,
+                      double a, double b, double c, int variant,
+                      void* workspace, size_t workspace_bytes, float* stats, void* stream);
+
+/*
+ * Phase timing, for benchmarks and profiling.  While enabled (process-wide),
+ * every kernel launch of the step entry points is bracketed by two HIP events
+ * recorded on the caller's stream.  muon_profile_read waits for the recorded
+ * events, adds each launch's elapsed milliseconds to ms_total[phase] and
+ * launches[phase] (arrays of nphases entries, host memory, zeroed by the
+ * caller), and forgets the records.  Phases: 0 head, 1 norm_finalize, 2 gram,
+ * 3 poly, 4 update, 5 tail_reduce, 6 tail_finalize, 7 tail_apply.
+ * Returns MUON_ERR_INVALID_ARGUMENT for null arrays or nphases < 1, and
+ * MUON_ERR_HIP if an event call failed.
+ */
+#define MUON_NUM_PHASES 8
+int muon_profile_enable(int enable);
+int muon_profile_read(double* ms_total, int64_t* launches, int nphases);
+/* Static name of a phase ("?" when out of range). */
+const char* muon_phase_name(int phase);
+
+/* Static string naming a status (never NULL). */
+const char* muon_status_string(int status);
+
+/* The HIP error code of the most recent MUON_ERR_HIP on this thread (0 if none). */
+int muon_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_MUON_H */

@@ -1,0 +1,280 @@
+"""PyTorch-facing binding of libmuon.so: tensor checks and argument marshalling.
+
+Every arithmetic step of the Muon step runs in the library's HIP kernels;
+PyTorch only provides device memory (weights, gradients, momentum, workspace,
+pointer tables) and the current stream.
+
+Defaults follow the pages: lr 0.02, momentum 0.95 with Nesterov, 5
+Newton-Schulz steps with (3.4445, -4.7750, 2.0315) ("LLM Pretraining Loss
+Spike 진단과 처방 ... Muon 전환 판단", section "Muon head의 실체는 하이브리드
+옵티마이저다"), weight decay 0.1 (the torch.optim.Muon example of "[Deep
+Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저", section 5), and
+non-2-D parameters are rejected (same section).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Iterable, Sequence
+
+import torch
+
+from . import _lib
+
+NS_COEFFICIENTS = (3.4445, -4.7750, 2.0315)
+VARIANTS = {"muon": _lib.MUON_VARIANT_MUON, "muongs": _lib.MUON_VARIANT_MUONGS}
+_DTYPES = {torch.float32: _lib.MUON_DTYPE_F32, torch.bfloat16: _lib.MUON_DTYPE_BF16}
+
+
+class MuonError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        msg = f"{where}: {_lib.status_string(status)} (status {status})"
+        if status == _lib.MUON_ERR_HIP:
+            msg += f", hip error {_lib.lib().muon_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.MUON_OK:
+        raise MuonError(status, where)
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    try:
+        return _DTYPES[dtype]
+    except KeyError:
+        raise TypeError(f"Muon weights must be float32 or bfloat16, got {dtype}") from None
+
+
+def _variant_code(variant) -> int:
+    if isinstance(variant, int):
+        return variant
+    try:
+        return VARIANTS[variant]
+    except KeyError:
+        raise ValueError(f"unknown variant {variant!r}; expected one of {sorted(VARIANTS)}") from None
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _scalars(dtype, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant):
+    a, b, c = ns_coefficients
+    return [dtype, float(lr), float(momentum), float(weight_decay), int(ns_steps),
+            float(a), float(b), float(c), _variant_code(variant)]
+
+
+def _check_matrix(name, t, shape=None, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.ndim != 2:
+        raise ValueError(f"Muon updates 2-D weight matrices only; {name} has {t.ndim} dims")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def workspace_bytes(count: int, rows: int, cols: int, dtype: torch.dtype) -> int:
+    return int(_lib.lib().muon_workspace_bytes(count, rows, cols, dtype_code(dtype)))
+
+
+def _groups_array(groups: Sequence[_lib.MuonGroup]):
+    arr = (_lib.MuonGroup * max(1, len(groups)))()
+    for i, g in enumerate(groups):
+        arr[i] = g
+    return arr
+
+
+def workspace_bytes_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype) -> int:
+    arr = _groups_array(groups)
+    return int(_lib.lib().muon_workspace_bytes_grouped(arr, len(groups), dtype_code(dtype)))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {nbytes} needed")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def muon_step(W, G, M, *, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
+              ns_coefficients=NS_COEFFICIENTS, variant="muon", workspace=None, stats=None,
+              stream=None):
+    """One Muon step on one matrix, in place on W and M.
+
+    W, G: [rows, cols] float32 or bfloat16 on the GPU (same dtype); M float32.
+    stats: optional float32 GPU tensor of 5 elements (||U||, ||W||^2, <W,O>,
+    ||O||^2, ||O~||^2).
+    """
+    _check_matrix("W", W)
+    _check_matrix("G", G, W.shape, W.dtype)
+    _check_matrix("M", M, W.shape, torch.float32)
+    rows, cols = W.shape
+    dt = dtype_code(W.dtype)
+    need = workspace_bytes(1, rows, cols, W.dtype)
+    ws = _workspace(need, W.device, workspace)
+    if stats is not None and (stats.dtype != torch.float32 or stats.numel() < 5 or not stats.is_cuda):
+        raise ValueError("stats must be a float32 GPU tensor with at least 5 elements")
+    st = _lib.lib().muon_step(
+        _ptr(W), _ptr(G), _ptr(M), rows, cols,
+        *_scalars(dt, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant),
+        _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
+    _check(st, "muon_step")
+    return W, M
+
+
+def pointer_table(tensors: Iterable[torch.Tensor], device) -> torch.Tensor:
+    """Device int64 array of the tensors' data pointers (a device pointer table)."""
+    ptrs = [t.data_ptr() for t in tensors]
+    return torch.tensor(ptrs, dtype=torch.int64, device=device)
+
+
+def muon_step_batched(Ws, Gs, Ms, *, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
+                      ns_coefficients=NS_COEFFICIENTS, variant="muon", workspace=None,
+                      stats=None, stream=None, tables=None):
+    """One Muon step on a list of same-shape matrices (device pointer tables).
+
+    ``tables`` may pass prebuilt (W, G, M) pointer tables to skip rebuilding.
+    """
+    Ws, Gs, Ms = list(Ws), list(Gs), list(Ms)
+    if not (len(Ws) == len(Gs) == len(Ms)):
+        raise ValueError("W, G and M lists must have the same length")
+    if not Ws:
+        return
+    shape, dtype = Ws[0].shape, Ws[0].dtype
+    for i, (w, g, m) in enumerate(zip(Ws, Gs, Ms)):
+        _check_matrix(f"W[{i}]", w, shape, dtype)
+        _check_matrix(f"G[{i}]", g, shape, dtype)
+        _check_matrix(f"M[{i}]", m, shape, torch.float32)
+    dev = Ws[0].device
+    if tables is None:
+        tables = (pointer_table(Ws, dev), pointer_table(Gs, dev), pointer_table(Ms, dev))
+    rows, cols = shape
+    need = workspace_bytes(len(Ws), rows, cols, dtype)
+    ws = _workspace(need, dev, workspace)
+    st = _lib.lib().muon_step_batched(
+        _ptr(tables[0]), _ptr(tables[1]), _ptr(tables[2]), len(Ws), rows, cols,
+        *_scalars(dtype_code(dtype), lr, momentum, weight_decay, ns_steps, ns_coefficients,
+                  variant),
+        _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
+    _check(st, "muon_step_batched")
+
+
+def stacked_group(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor) -> _lib.MuonGroup:
+    """A group over contiguous [count, rows, cols] stacks."""
+    if W.ndim != 3:
+        raise ValueError("a stacked group needs [count, rows, cols] tensors")
+    for name, t, dt in (("W", W, W.dtype), ("G", G, W.dtype), ("M", M, torch.float32)):
+        if tuple(t.shape) != tuple(W.shape) or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} stack must be a contiguous GPU tensor of shape "
+                             f"{tuple(W.shape)} and dtype {dt}")
+    n, r, c = W.shape
+    return _lib.MuonGroup(n, r, c, None, None, None, W.data_ptr(), G.data_ptr(), M.data_ptr())
+
+
+def table_group(count, rows, cols, W_table, G_table, M_table) -> _lib.MuonGroup:
+    """A group over device pointer tables (int64 GPU tensors of data pointers)."""
+    return _lib.MuonGroup(count, rows, cols, W_table.data_ptr(), G_table.data_ptr(),
+                          M_table.data_ptr(), None, None, None)
+
+
+def muon_step_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, lr=0.02,
+                      momentum=0.95, weight_decay=0.1, ns_steps=5,
+                      ns_coefficients=NS_COEFFICIENTS, variant="muon", workspace=None,
+                      stats=None, stream=None, device=None):
+    """One Muon step over several shape groups (a whole model) in one launch
+    sequence.  Build groups with :func:`stacked_group` / :func:`table_group`;
+    the caller keeps the tensors they point to alive."""
+    groups = list(groups)
+    need = workspace_bytes_grouped(groups, dtype)
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    ws = _workspace(need, device, workspace)
+    arr = _groups_array(groups)
+    st = _lib.lib().muon_step_grouped(
+        arr, len(groups),
+        *_scalars(dtype_code(dtype), lr, momentum, weight_decay, ns_steps, ns_coefficients,
+                  variant),
+        _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
+    _check(st, "muon_step_grouped")
+
+
+class MuonStep:
+    """Muon (or MuonGS) for a list of 2-D hidden weights.
+
+    Parameters are grouped by (shape, dtype); each group keeps device pointer
+    tables and fp32 momentum buffers, and :meth:`step` updates every group in
+    one launch sequence per dtype from the parameters' ``.grad``.
+    """
+
+    def __init__(self, params, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
+                 ns_coefficients=NS_COEFFICIENTS, variant="muon"):
+        self.params = list(params)
+        for i, p in enumerate(self.params):
+            if p.ndim != 2:
+                raise ValueError(f"Muon updates 2-D weight matrices only; parameter {i} has "
+                                 f"{p.ndim} dims (use AdamW for it)")
+            _check_matrix(f"param[{i}]", p.data)
+        self.hp = dict(lr=lr, momentum=momentum, weight_decay=weight_decay, ns_steps=ns_steps,
+                       ns_coefficients=tuple(ns_coefficients), variant=variant)
+        self.momentum_buffers = [torch.zeros(p.shape, dtype=torch.float32, device=p.device)
+                                 for p in self.params]
+        self._by_dtype = {}
+        for i, p in enumerate(self.params):
+            self._by_dtype.setdefault(p.dtype, {}).setdefault(tuple(p.shape), []).append(i)
+        self._tables = {}
+        self._workspaces = {}
+
+    def _groups(self, dtype, shapes):
+        groups, keep = [], []
+        for shape, idx in shapes.items():
+            dev = self.params[idx[0]].device
+            grads = []
+            for i in idx:
+                g = self.params[i].grad
+                if g is None:
+                    raise RuntimeError(f"parameter {i} has no gradient")
+                _check_matrix(f"grad[{i}]", g, shape, dtype)
+                grads.append(g)
+            key = (dtype, shape)
+            if key not in self._tables:
+                self._tables[key] = [pointer_table([self.params[i].data for i in idx], dev), None,
+                                     pointer_table([self.momentum_buffers[i] for i in idx], dev),
+                                     None]
+            tab = self._tables[key]
+            gptrs = tuple(g.data_ptr() for g in grads)
+            if tab[3] != gptrs:
+                tab[1] = pointer_table(grads, dev)
+                tab[3] = gptrs
+            groups.append(table_group(len(idx), shape[0], shape[1], tab[0], tab[1], tab[2]))
+            keep.append(grads)
+        return groups, keep
+
+    @torch.no_grad()
+    def step(self, stats=None):
+        for dtype, shapes in self._by_dtype.items():
+            groups, _keep = self._groups(dtype, shapes)
+            need = workspace_bytes_grouped(groups, dtype)
+            ws = self._workspaces.get(dtype)
+            if ws is None or ws.numel() < need:
+                dev = self.params[next(iter(shapes.values()))[0]].device
+                ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+                self._workspaces[dtype] = ws
+            muon_step_grouped(groups, dtype, workspace=ws, stats=stats, device=ws.device,
+                              **self.hp)

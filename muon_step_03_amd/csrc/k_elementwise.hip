@@ -1,0 +1,408 @@
+// Elementwise phases of the Muon step: the head (momentum, Nesterov
+// look-ahead, Frobenius-norm partials, X0 write in short-side orientation)
+// and the tail (MuonGS reductions, projection, RMS scale, decoupled weight
+// decay, W update).  Both are HBM-bound; each block moves one 64x64 tile with
+// coalesced accesses, transposing through LDS when a tall matrix is iterated
+// as its transpose.
+//
+// Passages: update order — "[Deep Learning] Muon — 행렬 업데이트를 직교화하는
+// 옵티마이저", section 3; SGD-momentum/Nesterov defaults and the 1e-7
+// normaliser — "LLM Pretraining Loss Spike 진단과 처방 ... Muon 전환 판단",
+// section "Muon head의 실체는 하이브리드 옵티마이저다"; 0.2*sqrt(max(A,B)) —
+// "[논문 AI 리뷰] MUON IS SCALABLE FOR LLM TRAINING", section 2, eq. 4;
+// Gram-Schmidt projection — "MuonGS: Pretraining LLMs with Relaxed
+// Weight-Norm Control", section "전제와 한계".
+#include "muon_internal.h"
+
+namespace muon {
+namespace {
+
+constexpr int T = kEwTile;  // 64
+
+struct TileRef {
+  const MatGroup* g;
+  int64_t m;     // matrix index within the group
+  int tile;      // tile index within the matrix
+};
+
+__device__ __forceinline__ TileRef decode(const Batch& bt, const Work& wk) {
+  const int64_t bid = blockIdx.x;
+  const int gi = find_group(wk, bid);
+  const int64_t local = bid - wk.begin[gi];
+  const int tiles = wk.tiles[gi];
+  TileRef r;
+  r.g = &bt.g[gi];
+  r.m = local / tiles;
+  r.tile = int(local - r.m * tiles);
+  return r;
+}
+
+__device__ __forceinline__ bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+template <bool BF16>
+struct Vec4;
+template <>
+struct Vec4<true> {  // 4 bf16 = 8 bytes
+  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
+    const uint2 d = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(d.x << 16);
+    v[1] = __uint_as_float(d.x & 0xffff0000u);
+    v[2] = __uint_as_float(d.y << 16);
+    v[3] = __uint_as_float(d.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
+    uint2 d;
+    d.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+    d.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = d;
+  }
+};
+template <>
+struct Vec4<false> {  // 4 floats = 16 bytes
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    const float4 d = *reinterpret_cast<const float4*>(p);
+    v[0] = d.x; v[1] = d.y; v[2] = d.z; v[3] = d.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// ------------------------------------------------------------------- head
+// M' = mu*M + G, U = G + mu*M' on one 64x64 tile of X (X = U, or U^T for a
+// tall matrix); writes M' in place, U (rounded to X's type) into X0 with
+// zeros in the padding, and the tile's sum of u^2 (fp32, unrounded u).
+template <bool BF16>
+__global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) {
+  using E = Elem<BF16>;
+  using TE = typename E::T;
+  __shared__ float S[T][T + 1];
+  __shared__ float red[4];
+
+  const TileRef tr = decode(bt, wk);
+  const MatGroup& g = *tr.g;
+  const int ntj = g.q_pad / T;
+  const int ti = tr.tile / ntj;
+  const int tj = tr.tile - ti * ntj;
+  const int i0 = ti * T, j0 = tj * T;            // X-orientation origin
+  const int sr0 = g.trans ? j0 : i0;             // weight-orientation origin
+  const int sc0 = g.trans ? i0 : j0;
+  const int64_t elems = int64_t(g.rows) * g.cols;
+  const TE* G = mat_cptr<TE>(g.G_tab, g.G, tr.m, elems);
+  float* M = mat_ptr<float>(reinterpret_cast<void* const*>(g.M_tab),
+                            reinterpret_cast<char*>(g.M), tr.m, elems);
+  TE* X = reinterpret_cast<TE*>(g.X0) + tr.m * g.x_stride;
+
+  const int t = threadIdx.x;
+  const int rb = t >> 4;          // 0..15
+  const int cq = (t & 15) * 4;    // 0..60
+  const bool vec = (sc0 + T <= g.cols) && ((g.cols & 3) == 0) && aligned16(M) &&
+                   ((reinterpret_cast<uintptr_t>(G) & (BF16 ? 7u : 15u)) == 0);
+
+  float u[4][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = sr0 + rb + 16 * k;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[k][e] = 0.f;
+    if (r < g.rows) {
+      const int64_t off = int64_t(r) * g.cols + sc0 + cq;
+      if (vec) {
+        float gv[4], mv[4];
+        Vec4<BF16>::load(G + off, gv);
+        Vec4<false>::load(M + off, mv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mv[e] = fmaf(mu, mv[e], gv[e]);
+          u[k][e] = fmaf(mu, mv[e], gv[e]);
+        }
+        Vec4<false>::store(M + off, mv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (sc0 + cq + e < g.cols) {
+            const float gv = E::load(G + off + e);
+            const float mv = fmaf(mu, M[off + e], gv);
+            M[off + e] = mv;
+            u[k][e] = fmaf(mu, mv, gv);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(u[k][e], u[k][e], ss);
+  }
+
+  if (!g.trans) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      Vec4<BF16>::store(X + int64_t(i0 + rb + 16 * k) * g.q_pad + j0 + cq, u[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[rb + 16 * k][cq + e] = u[k][e];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int xi = rb + 16 * k;  // X row offset = source column offset
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = S[cq + e][xi];
+      Vec4<BF16>::store(X + int64_t(i0 + xi) * g.q_pad + j0 + cq, v);
+    }
+  }
+
+  const float tot = block_sum_256(ss, red);
+  if (t == 0) g.head_part[tr.m * g.head_tiles + tr.tile] = tot;
+}
+
+// ||U||_F from the head partials of one matrix (one block per matrix, fixed
+// summation order).
+__global__ __launch_bounds__(256) void norm_finalize_kernel(Batch bt, Work wk) {
+  __shared__ float red[4];
+  const TileRef tr = decode(bt, wk);
+  const MatGroup& g = *tr.g;
+  const float* part = g.head_part + tr.m * g.head_tiles;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < g.head_tiles; i += 256) s += part[i];
+  s = block_sum_256(s, red);
+  if (threadIdx.x == 0) {
+    const float n = sqrtf(s);
+    float* sc = g.scal + tr.m * kScal;
+    sc[SC_NORM] = n;
+    sc[SC_INV] = 1.0f / (n + kEps);
+    if (g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 0] = n;
+  }
+}
+
+// ------------------------------------------------------------------- tail
+// Gathers, for the thread's 4x4 elements of a 64x64 weight tile at (r0, c0),
+// the Newton-Schulz output O in weight orientation (through LDS when the
+// iterate is the transpose).  Every X access lies inside the padded extents.
+template <bool BF16>
+__device__ __forceinline__ void load_o_tile(const MatGroup& g, const typename Elem<BF16>::T* X,
+                                            int r0, int c0, float (*S)[T + 1], float o[4][4]) {
+  const int t = threadIdx.x;
+  const int rb = t >> 4, cq = (t & 15) * 4;
+  if (!g.trans) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      Vec4<BF16>::load(X + int64_t(r0 + rb + 16 * k) * g.q_pad + c0 + cq, o[k]);
+  } else {
+    // X rows are weight columns: read X[c0 + i][r0 + j] coalesced, then
+    // transpose through LDS.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float v[4];
+      Vec4<BF16>::load(X + int64_t(c0 + rb + 16 * k) * g.q_pad + r0 + cq, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[rb + 16 * k][cq + e] = v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[k][e] = S[cq + e][rb + 16 * k];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_w_tile(const MatGroup& g, const typename Elem<BF16>::T* W,
+                                            int r0, int c0, float w[4][4], bool valid[4][4]) {
+  using E = Elem<BF16>;
+  const int t = threadIdx.x;
+  const int rb = t >> 4, cq = (t & 15) * 4;
+  const bool vec = (c0 + T <= g.cols) && ((g.cols & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(W) & (BF16 ? 7u : 15u)) == 0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + rb + 16 * k;
+    const int64_t off = int64_t(r) * g.cols + c0 + cq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[k][e] = 0.f;
+      valid[k][e] = (r < g.rows) && (c0 + cq + e < g.cols);
+    }
+    if (r < g.rows) {
+      if (vec) {
+        Vec4<BF16>::load(W + off, w[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (valid[k][e]) w[k][e] = E::load(W + off + e);
+      }
+    }
+  }
+}
+
+// Per-tile partials of <W,O>, ||W||^2, ||O||^2 (O scaled by 1/(||U||+eps)
+// when no Newton-Schulz step ran, since X0 holds the unnormalised U).
+template <bool BF16>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int ns_steps) {
+  using TE = typename Elem<BF16>::T;
+  __shared__ float S[T][T + 1];
+  __shared__ float red[4];
+  const TileRef tr = decode(bt, wk);
+  const MatGroup& g = *tr.g;
+  const int tr_ = tr.tile / g.tail_tiles_c;
+  const int tc_ = tr.tile - tr_ * g.tail_tiles_c;
+  const int r0 = tr_ * T, c0 = tc_ * T;
+  const int64_t elems = int64_t(g.rows) * g.cols;
+  const TE* W = mat_cptr<TE>(reinterpret_cast<const void* const*>(g.W_tab), g.W, tr.m, elems);
+  const TE* X = reinterpret_cast<const TE*>((ns_steps & 1) ? g.X1 : g.X0) + tr.m * g.x_stride;
+  const float oscale = ns_steps == 0 ? g.scal[tr.m * kScal + SC_INV] : 1.0f;
+
+  float w[4][4], o[4][4];
+  bool valid[4][4];
+  load_w_tile<BF16>(g, W, r0, c0, w, valid);
+  load_o_tile<BF16>(g, X, r0, c0, S, o);
+  float dot = 0.f, ww = 0.f, oo = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ov = valid[k][e] ? o[k][e] * oscale : 0.f;
+      dot = fmaf(w[k][e], ov, dot);
+      ww = fmaf(w[k][e], w[k][e], ww);
+      oo = fmaf(ov, ov, oo);
+    }
+  dot = block_sum_256(dot, red);
+  ww = block_sum_256(ww, red);
+  oo = block_sum_256(oo, red);
+  if (threadIdx.x == 0) {
+    float* p = g.tail_part + (tr.m * g.tail_tiles + tr.tile) * 3;
+    p[0] = dot;
+    p[1] = ww;
+    p[2] = oo;
+  }
+}
+
+// Per-matrix totals: ||W||^2, <W,O>, ||O||^2, the MuonGS coefficient and the
+// optional stats.
+__global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, int variant) {
+  __shared__ float red[4];
+  const TileRef tr = decode(bt, wk);
+  const MatGroup& g = *tr.g;
+  const float* part = g.tail_part + tr.m * g.tail_tiles * 3;
+  float dot = 0.f, ww = 0.f, oo = 0.f;
+  for (int i = threadIdx.x; i < g.tail_tiles; i += 256) {
+    dot += part[3 * i + 0];
+    ww += part[3 * i + 1];
+    oo += part[3 * i + 2];
+  }
+  dot = block_sum_256(dot, red);
+  ww = block_sum_256(ww, red);
+  oo = block_sum_256(oo, red);
+  if (threadIdx.x == 0) {
+    const float coef = (variant == MUON_VARIANT_MUONGS && ww > 0.f) ? dot / ww : 0.f;
+    float* sc = g.scal + tr.m * kScal;
+    sc[SC_R2] = ww;
+    sc[SC_DOT] = dot;
+    sc[SC_O2] = oo;
+    sc[SC_COEF] = coef;
+    if (g.stats) {
+      float* st = g.stats + tr.m * MUON_STATS_PER_MATRIX;
+      st[1] = ww;
+      st[2] = dot;
+      st[3] = oo;
+      st[4] = fmaxf(oo - 2.f * coef * dot + coef * coef * ww, 0.f);
+    }
+  }
+}
+
+// W' = (1 - lr*wd) W - lr*s*(O - coef*W), s = 0.2*sqrt(max(rows, cols)).
+template <bool BF16>
+__global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int ns_steps,
+                                                         int use_coef) {
+  using E = Elem<BF16>;
+  using TE = typename E::T;
+  __shared__ float S[T][T + 1];
+  const TileRef tr = decode(bt, wk);
+  const MatGroup& g = *tr.g;
+  const int tr_ = tr.tile / g.tail_tiles_c;
+  const int tc_ = tr.tile - tr_ * g.tail_tiles_c;
+  const int r0 = tr_ * T, c0 = tc_ * T;
+  const int64_t elems = int64_t(g.rows) * g.cols;
+  TE* W = mat_ptr<TE>(g.W_tab, g.W, tr.m, elems);
+  const TE* X = reinterpret_cast<const TE*>((ns_steps & 1) ? g.X1 : g.X0) + tr.m * g.x_stride;
+  const float* sc = g.scal + tr.m * kScal;
+  const float oscale = ns_steps == 0 ? sc[SC_INV] : 1.0f;
+  const float coef = use_coef ? sc[SC_COEF] : 0.f;
+  const float step = g.step;
+  const float wcoef = g.decay + step * coef;
+  const float ocoef = step * oscale;
+
+  float w[4][4], o[4][4];
+  bool valid[4][4];
+  load_w_tile<BF16>(g, W, r0, c0, w, valid);
+  load_o_tile<BF16>(g, X, r0, c0, S, o);
+
+  const int t = threadIdx.x;
+  const int rb = t >> 4, cq = (t & 15) * 4;
+  const bool vec = (c0 + T <= g.cols) && ((g.cols & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(W) & (BF16 ? 7u : 15u)) == 0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + rb + 16 * k;
+    if (r >= g.rows) continue;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = fmaf(wcoef, w[k][e], -ocoef * o[k][e]);
+    const int64_t off = int64_t(r) * g.cols + c0 + cq;
+    if (vec) {
+      Vec4<BF16>::store(W + off, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid[k][e]) W[off + e] = E::cvt(v[e]);
+    }
+  }
+}
+
+inline dim3 grid_of(const Work& wk) { return dim3(unsigned(wk.begin[wk.ngroups])); }
+
+}  // namespace
+
+hipError_t launch_head(const Batch& bt, const Work& wk, bool bf16, float momentum, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(head_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, momentum);
+  else
+    hipLaunchKernelGGL(head_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, momentum);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const Batch& bt, const Work& wk, hipStream_t s) {
+  hipLaunchKernelGGL(norm_finalize_kernel, grid_of(wk), dim3(256), 0, s, bt, wk);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps,
+                              hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(tail_reduce_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, ns_steps);
+  else
+    hipLaunchKernelGGL(tail_reduce_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, ns_steps);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s) {
+  hipLaunchKernelGGL(tail_finalize_kernel, grid_of(wk), dim3(256), 0, s, bt, wk, variant);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,
+                             bool coef, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(tail_apply_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, h.ns_steps,
+                       int(coef));
+  else
+    hipLaunchKernelGGL(tail_apply_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, h.ns_steps,
+                       int(coef));
+  return hipGetLastError();
+}
+
+}  // namespace muon

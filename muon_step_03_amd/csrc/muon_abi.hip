@@ -1,0 +1,476 @@
+// C ABI of the Muon step: argument validation, workspace layout and the
+// launch sequence on the caller's stream.  Every argument is checked before
+// the first HIP call, so every error status is returned without touching the
+// device.
+//
+// Launch sequence for one set of up to MUON_GROUPS_PER_LAUNCH shape groups
+// (each phase is ONE launch over the tiles of every matrix of every group):
+//   head            M' = mu M + G, U = G + mu M', X0 = U (short side first),
+//                   per-tile sums of u^2
+//   norm_finalize   ||U||_F and 1/(||U||_F + 1e-7) per matrix
+//   ns_steps x { gram, poly, update }
+//   tail_reduce + tail_finalize   (MuonGS or stats only) <W,O>, ||W||^2, ||O||^2
+//   tail_apply      W' = (1 - lr wd) W - lr s O~
+// Update order: "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저",
+// section 3 "Muon의 업데이트 순서".
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
+
+inline bool mul_ok(size_t a, size_t b, size_t* out) { return !__builtin_mul_overflow(a, b, out); }
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+bool debug_sync() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("MUON_DEBUG");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+bool dtype_ok(int dtype) { return dtype == MUON_DTYPE_F32 || dtype == MUON_DTYPE_BF16; }
+
+struct Layout {
+  int64_t p, q, p_pad, q_pad;
+  int trans;
+  int64_t head_tiles, tail_tiles, tail_tiles_c;
+  int64_t tile;             // NS GEMM block tile edge
+  size_t x_bytes, a_bytes, head_bytes, tail_bytes, scal_bytes;
+  size_t total;             // 0 on overflow
+};
+
+Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
+  Layout L{};
+  const size_t es = dtype == MUON_DTYPE_BF16 ? 2 : 4;
+  L.tile = dtype == MUON_DTYPE_BF16 ? kBf16Tile : kF32Tile;
+  L.trans = rows > cols ? 1 : 0;
+  L.p = rows < cols ? rows : cols;
+  L.q = rows < cols ? cols : rows;
+  L.p_pad = round_up(L.p, L.tile);
+  L.q_pad = round_up(L.q, L.tile);
+  L.head_tiles = (L.p_pad / kEwTile) * (L.q_pad / kEwTile);
+  L.tail_tiles_c = cdiv(cols, kEwTile);
+  L.tail_tiles = cdiv(rows, kEwTile) * L.tail_tiles_c;
+  size_t x, a, h, t, s;
+  const size_t c = size_t(count);
+  if (!mul_ok(c, size_t(L.p_pad * L.q_pad) * es, &x) || !mul_ok(c, size_t(L.p_pad * L.p_pad) * es, &a) ||
+      !mul_ok(c, size_t(L.head_tiles) * 4, &h) || !mul_ok(c, size_t(L.tail_tiles) * 12, &t) ||
+      !mul_ok(c, size_t(kScal) * 4, &s))
+    return L;  // total stays 0
+  L.x_bytes = align_up(x);
+  L.a_bytes = align_up(a);
+  L.head_bytes = align_up(h);
+  L.tail_bytes = align_up(t);
+  L.scal_bytes = align_up(s);
+  L.total = 2 * L.x_bytes + 2 * L.a_bytes + L.head_bytes + L.tail_bytes + L.scal_bytes;
+  if (L.total < L.x_bytes) L.total = 0;
+  return L;
+}
+
+int check_scalars(double lr, double momentum, double wd, int ns_steps, double a, double b,
+                  double c, int variant) {
+  if (!std::isfinite(lr) || !std::isfinite(momentum) || !std::isfinite(wd) ||
+      !std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
+    return MUON_ERR_INVALID_ARGUMENT;
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS) return MUON_ERR_INVALID_ARGUMENT;
+  if (variant != MUON_VARIANT_MUON && variant != MUON_VARIANT_MUONGS)
+    return MUON_ERR_INVALID_ARGUMENT;
+  return MUON_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_group(const muon_group& g, int dtype) {
+  if (g.count < 0) return MUON_ERR_INVALID_ARGUMENT;
+  if (g.count == 0) return MUON_OK;
+  if (g.rows < 1 || g.cols < 1 || g.rows > MUON_MAX_DIM || g.cols > MUON_MAX_DIM)
+    return MUON_ERR_INVALID_SHAPE;
+  const bool any_tab = g.W_table || g.G_table || g.M_table;
+  const bool any_stk = g.W || g.G || g.M;
+  if (any_tab == any_stk) return MUON_ERR_INVALID_ARGUMENT;  // neither form, or both
+  if (any_tab && !(g.W_table && g.G_table && g.M_table)) return MUON_ERR_INVALID_ARGUMENT;
+  if (any_stk) {
+    if (!(g.W && g.G && g.M)) return MUON_ERR_INVALID_ARGUMENT;
+    const size_t es = dtype == MUON_DTYPE_BF16 ? 2 : 4;
+    size_t n;
+    if (!mul_ok(size_t(g.count), size_t(g.rows) * size_t(g.cols), &n)) return MUON_ERR_INVALID_SHAPE;
+    if (ranges_overlap(g.W, n * es, g.G, n * es) || ranges_overlap(g.W, n * es, g.M, n * 4) ||
+        ranges_overlap(g.G, n * es, g.M, n * 4))
+      return MUON_ERR_INVALID_ARGUMENT;
+  }
+  return MUON_OK;
+}
+
+// Blocks per matrix of each phase.
+struct PhaseTiles {
+  int64_t head, gram, update, tail;
+};
+PhaseTiles phase_tiles(const Layout& L) {
+  PhaseTiles t;
+  const int64_t nt = L.p_pad / L.tile;
+  t.head = L.head_tiles;
+  t.gram = nt * (nt + 1) / 2;
+  t.update = nt * (L.q_pad / L.tile);
+  t.tail = L.tail_tiles;
+  return t;
+}
+
+const char* kPhaseNames[] = {"head", "norm_finalize", "gram", "poly", "update",
+                             "tail_reduce", "tail_finalize", "tail_apply"};
+
+// ---- optional phase timing (HIP events around each launch)
+struct ProfRecord {
+  int phase;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records the start event of a launch when profiling is on.
+hipEvent_t prof_start(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return nullptr;
+  hipEvent_t e = pooled_event();
+  if (e && hipEventRecord(e, s) != hipSuccess) {
+    g_event_pool.push_back(e);
+    return nullptr;
+  }
+  return e;
+}
+
+void prof_stop(hipEvent_t start, int phase, hipStream_t s) {
+  if (!start) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t e = pooled_event();
+  if (!e || hipEventRecord(e, s) != hipSuccess) {
+    g_event_pool.push_back(start);
+    if (e) g_event_pool.push_back(e);
+    return;
+  }
+  g_prof_records.push_back({phase, start, e});
+}
+
+int finish_launch(hipError_t e, int phase, hipStream_t s, hipEvent_t t0 = nullptr) {
+  prof_stop(t0, phase, s);
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    g_last_hip_error = int(e);
+    if (debug_sync())
+      std::fprintf(stderr, "muon: %s failed: %s\n", kPhaseNames[phase], hipGetErrorString(e));
+    return MUON_ERR_HIP;
+  }
+  return MUON_OK;
+}
+
+struct Sel {
+  const muon_group* g;
+  Layout L;
+  int64_t stats_index;  // first matrix of the group in the stats array
+};
+
+int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, double momentum,
+               double wd, int ns_steps, double a, double b, double c, int variant,
+               void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  if (!dtype_ok(dtype)) return MUON_ERR_UNSUPPORTED_DTYPE;
+  int st = check_scalars(lr, momentum, wd, ns_steps, a, b, c, variant);
+  if (st != MUON_OK) return st;
+  if (ngroups < 0 || (ngroups > 0 && !groups)) return MUON_ERR_INVALID_ARGUMENT;
+
+  size_t need = 0;
+  int64_t n_matrices = 0;
+  int64_t blocks = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    st = check_group(groups[i], dtype);
+    if (st != MUON_OK) return st;
+    if (groups[i].count == 0) continue;
+    const Layout L = make_layout(groups[i].count, groups[i].rows, groups[i].cols, dtype);
+    if (L.total == 0) return MUON_ERR_INVALID_SHAPE;
+    const PhaseTiles pt = phase_tiles(L);
+    int64_t most = pt.head > pt.update ? pt.head : pt.update;
+    most = most > pt.tail ? most : pt.tail;
+    // The dispatch grid is counted in work-items (32 bits): at 256 threads a
+    // block, one launch holds fewer than 2^24 blocks.
+    if (groups[i].count > kMaxBlocks / most) return MUON_ERR_INVALID_SHAPE;
+    blocks += groups[i].count * most;
+    if (blocks > kMaxBlocks) return MUON_ERR_INVALID_SHAPE;
+    need += L.total;
+    n_matrices += groups[i].count;
+  }
+  if (n_matrices == 0) return MUON_OK;  // empty batch: nothing to do
+  need += kAlign;
+  if (!workspace) return MUON_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  for (int i = 0; i < ngroups; ++i) {
+    const muon_group& g = groups[i];
+    if (g.count == 0 || !g.W) continue;
+    const size_t es = dtype == MUON_DTYPE_BF16 ? 2 : 4;
+    const size_t n = size_t(g.count) * size_t(g.rows) * size_t(g.cols);
+    if (ranges_overlap(workspace, workspace_bytes, g.W, n * es) ||
+        ranges_overlap(workspace, workspace_bytes, g.G, n * es) ||
+        ranges_overlap(workspace, workspace_bytes, g.M, n * 4))
+      return MUON_ERR_INVALID_ARGUMENT;
+  }
+
+  // ---- all arguments valid: enqueue work
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear an unrelated earlier error
+  const bool bf16 = dtype == MUON_DTYPE_BF16;
+  char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+  Hyper h;
+  h.lr = float(lr);
+  h.momentum = float(momentum);
+  h.wd = float(wd);
+  h.a = float(a);
+  h.b = float(b);
+  h.c = float(c);
+  h.ns_steps = ns_steps;
+  h.variant = variant;
+  const bool reduce = variant == MUON_VARIANT_MUONGS || stats != nullptr;
+
+  Sel sel[kMaxGroups];
+  int nsel = 0;
+  int64_t stats_index = 0;
+  int gi = 0;
+  while (gi < ngroups) {
+    nsel = 0;
+    for (; gi < ngroups && nsel < kMaxGroups; ++gi) {
+      if (groups[gi].count == 0) continue;
+      sel[nsel].g = &groups[gi];
+      sel[nsel].L = make_layout(groups[gi].count, groups[gi].rows, groups[gi].cols, dtype);
+      sel[nsel].stats_index = stats_index;
+      stats_index += groups[gi].count;
+      ++nsel;
+    }
+    if (nsel == 0) break;
+
+    Batch bt;
+    std::memset(&bt, 0, sizeof(bt));
+    bt.ngroups = nsel;
+    Work w_head{}, w_one{}, w_gram{}, w_upd{}, w_tail{};
+    w_head.ngroups = w_one.ngroups = w_gram.ngroups = w_upd.ngroups = w_tail.ngroups = nsel;
+    for (int k = 0; k < nsel; ++k) {
+      const muon_group& u = *sel[k].g;
+      const Layout& L = sel[k].L;
+      MatGroup& m = bt.g[k];
+      m.W_tab = u.W_table;
+      m.G_tab = u.G_table;
+      m.M_tab = u.M_table;
+      m.W = static_cast<char*>(u.W);
+      m.G = static_cast<const char*>(u.G);
+      m.M = u.M;
+      m.count = u.count;
+      m.rows = int(u.rows);
+      m.cols = int(u.cols);
+      m.p = int(L.p);
+      m.q = int(L.q);
+      m.p_pad = int(L.p_pad);
+      m.q_pad = int(L.q_pad);
+      m.trans = L.trans;
+      m.head_tiles = int(L.head_tiles);
+      m.tail_tiles = int(L.tail_tiles);
+      m.tail_tiles_c = int(L.tail_tiles_c);
+      m.X0 = base;
+      base += L.x_bytes;
+      m.X1 = base;
+      base += L.x_bytes;
+      m.A = base;
+      base += L.a_bytes;
+      m.B = base;
+      base += L.a_bytes;
+      m.x_stride = L.p_pad * L.q_pad;
+      m.a_stride = L.p_pad * L.p_pad;
+      m.head_part = reinterpret_cast<float*>(base);
+      base += L.head_bytes;
+      m.tail_part = reinterpret_cast<float*>(base);
+      base += L.tail_bytes;
+      m.scal = reinterpret_cast<float*>(base);
+      base += L.scal_bytes;
+      m.stats = stats ? stats + sel[k].stats_index * MUON_STATS_PER_MATRIX : nullptr;
+      m.decay = float(1.0 - lr * wd);
+      m.step = float(lr * 0.2 * std::sqrt(double(L.q)));
+
+      const PhaseTiles pt = phase_tiles(L);
+      w_head.tiles[k] = int(pt.head);
+      w_one.tiles[k] = 1;
+      w_gram.tiles[k] = int(pt.gram);
+      w_upd.tiles[k] = int(pt.update);
+      w_tail.tiles[k] = int(pt.tail);
+    }
+    hipEvent_t t0 = nullptr;
+    Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};
+    for (Work* w : ws) {
+      w->begin[0] = 0;
+      for (int k = 0; k < nsel; ++k) w->begin[k + 1] = w->begin[k] + bt.g[k].count * w->tiles[k];
+    }
+
+    if ((t0 = prof_start(s)), (st = finish_launch(launch_head(bt, w_head, bf16, h.momentum, s), 0, s, t0))) return st;
+    if ((t0 = prof_start(s)), (st = finish_launch(launch_norm_finalize(bt, w_one, s), 1, s, t0))) return st;
+    for (int it = 0; it < ns_steps; ++it) {
+      if (bf16) {
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, w_gram, it, s), 2, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, w_upd, it, h.a, s), 4, s, t0))) return st;
+      } else {
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_f32(bt, w_gram, it, s), 2, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_f32(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_f32(bt, w_upd, it, h.a, s), 4, s, t0))) return st;
+      }
+    }
+    if (reduce) {
+      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, s), 5, s, t0))) return st;
+      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, variant, s), 6, s, t0))) return st;
+    }
+    if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h,
+                                                                     variant == MUON_VARIANT_MUONGS, s),
+                                                   7, s, t0)))
+      return st;
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muon_workspace_bytes(int64_t count, int64_t rows, int64_t cols, int dtype) {
+  if (!dtype_ok(dtype) || count < 0) return 0;
+  if (count == 0) return 0;
+  if (rows < 1 || cols < 1 || rows > MUON_MAX_DIM || cols > MUON_MAX_DIM) return 0;
+  const Layout L = make_layout(count, rows, cols, dtype);
+  return L.total ? L.total + kAlign : 0;
+}
+
+size_t muon_workspace_bytes_grouped(const muon_group* groups, int ngroups, int dtype) {
+  if (!dtype_ok(dtype) || ngroups < 0 || (ngroups > 0 && !groups)) return 0;
+  size_t need = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    const muon_group& g = groups[i];
+    if (g.count < 0) return 0;
+    if (g.count == 0) continue;
+    if (g.rows < 1 || g.cols < 1 || g.rows > MUON_MAX_DIM || g.cols > MUON_MAX_DIM) return 0;
+    const Layout L = make_layout(g.count, g.rows, g.cols, dtype);
+    if (!L.total) return 0;
+    need += L.total;
+  }
+  return need ? need + kAlign : 0;
+}
+
+int muon_step(void* W, const void* G, float* M, int64_t rows, int64_t cols, int dtype, double lr,
+              double momentum, double weight_decay, int ns_steps, double a, double b, double c,
+              int variant, void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  if (!W || !G || !M) return MUON_ERR_INVALID_ARGUMENT;
+  muon_group g{};
+  g.count = 1;
+  g.rows = rows;
+  g.cols = cols;
+  g.W = W;
+  g.G = G;
+  g.M = M;
+  return run_groups(&g, 1, dtype, lr, momentum, weight_decay, ns_steps, a, b, c, variant,
+                    workspace, workspace_bytes, stats, stream);
+}
+
+int muon_step_batched(void* const* W, const void* const* G, float* const* M, int64_t count,
+                      int64_t rows, int64_t cols, int dtype, double lr, double momentum,
+                      double weight_decay, int ns_steps, double a, double b, double c, int variant,
+                      void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  if (count < 0) return MUON_ERR_INVALID_ARGUMENT;
+  if (count > 0 && (!W || !G || !M)) return MUON_ERR_INVALID_ARGUMENT;
+  muon_group g{};
+  g.count = count;
+  g.rows = rows;
+  g.cols = cols;
+  g.W_table = W;
+  g.G_table = G;
+  g.M_table = M;
+  return run_groups(&g, 1, dtype, lr, momentum, weight_decay, ns_steps, a, b, c, variant,
+                    workspace, workspace_bytes, stats, stream);
+}
+
+int muon_step_grouped(const muon_group* groups, int ngroups, int dtype, double lr, double momentum,
+                      double weight_decay, int ns_steps, double a, double b, double c, int variant,
+                      void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  return run_groups(groups, ngroups, dtype, lr, momentum, weight_decay, ns_steps, a, b, c,
+                    variant, workspace, workspace_bytes, stats, stream);
+}
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MUON_ERR_INVALID_SHAPE: return "invalid shape";
+    case MUON_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MUON_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int muon_last_hip_error(void) { return g_last_hip_error; }
+
+int muon_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return MUON_OK;
+}
+
+int muon_profile_read(double* ms_total, int64_t* launches, int nphases) {
+  if (!ms_total || !launches || nphases < 1) return MUON_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int status = MUON_OK;
+  for (const ProfRecord& r : g_prof_records) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) {
+      g_last_hip_error = int(e);
+      status = MUON_ERR_HIP;
+    } else if (r.phase < nphases) {
+      ms_total[r.phase] += ms;
+      launches[r.phase] += 1;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof_records.clear();
+  return status;
+}
+
+const char* muon_phase_name(int phase) {
+  return (phase >= 0 && phase < MUON_NUM_PHASES) ? kPhaseNames[phase] : "?";
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Internal structures shared by the host dispatcher and the HIP kernels.
+//
+// Data layout in HBM (per shape group; every region 256-byte aligned):
+//   X0, X1  [count][p_pad][q_pad]   Newton-Schulz iterate, ping-pong.  X is
+//                                   the momentum look-ahead U in "short side
+//                                   first" orientation: X = U if rows <= cols,
+//                                   X = U^T otherwise.  Rows/cols beyond p/q
+//                                   are zero, and stay zero under the
+//                                   iteration, so the GEMM kernels need no
+//                                   edge masking.
+//   A, B    [count][p_pad][p_pad]   Gram matrix X X^T and polynomial b A + c A A
+//   head    [count][head_tiles]     per-tile partial sums of u^2
+//   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
+//   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
+// Element type of X, A, B is bf16 (bit pattern in uint16_t) on the bf16 path
+// and float on the fp32 path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon.h"
+
+namespace muon {
+
+constexpr int kMaxGroups = MUON_GROUPS_PER_LAUNCH;
+constexpr int kEwTile = 64;        // head/tail tile edge (elements)
+constexpr int kBf16Tile = 128;     // bf16 MFMA GEMM block tile edge
+constexpr int kF32Tile = 64;       // fp32 GEMM block tile edge
+constexpr float kEps = 1e-7f;      // added to ||U||_F before dividing
+
+// Per-matrix scalar slots.
+enum : int {
+  SC_NORM = 0,   // ||U||_F
+  SC_INV = 1,    // 1 / (||U||_F + eps)
+  SC_R2 = 2,     // ||W||_F^2
+  SC_DOT = 3,    // <W, O>_F
+  SC_O2 = 4,     // ||O||_F^2
+  SC_COEF = 5,   // MuonGS projection coefficient <W,O>/||W||^2 (0 for Muon)
+  kScal = 8
+};
+
+// One shape group as the kernels see it.
+struct MatGroup {
+  void* const* W_tab;
+  const void* const* G_tab;
+  float* const* M_tab;
+  char* W;
+  const char* G;
+  float* M;
+  int64_t count;
+  int rows, cols;      // weight orientation
+  int p, q;            // short side, long side
+  int p_pad, q_pad;    // padded X extents
+  int trans;           // 1 when rows > cols (X = U^T)
+  int head_tiles;      // head tiles per matrix (X orientation, 64x64)
+  int tail_tiles;      // tail tiles per matrix (W orientation, 64x64)
+  int tail_tiles_c;    // tail tiles along cols
+  char* X0;
+  char* X1;
+  char* A;
+  char* B;
+  int64_t x_stride;    // elements between matrices in X0/X1
+  int64_t a_stride;    // elements between matrices in A/B
+  float* head_part;
+  float* tail_part;
+  float* scal;
+  float* stats;        // MUON_STATS_PER_MATRIX per matrix, or null
+  float decay;         // 1 - lr*wd
+  float step;          // lr * 0.2 * sqrt(max(rows, cols))
+};
+
+struct Batch {
+  MatGroup g[kMaxGroups];
+  int ngroups;
+};
+
+// How one launch splits into blocks: `tiles[g]` blocks per matrix of group g,
+// blocks of group g are [begin[g], begin[g+1]).
+struct Work {
+  int64_t begin[kMaxGroups + 1];
+  int tiles[kMaxGroups];
+  int ngroups;
+};
+
+struct Hyper {
+  float lr;
+  float momentum;
+  float wd;
+  float a, b, c;
+  int ns_steps;
+  int variant;
+};
+
+// ---------------------------------------------------------------- device side
+__device__ __forceinline__ int find_group(const Work& w, int64_t bid) {
+  int g = 0;
+  while (g + 1 < w.ngroups && bid >= w.begin[g + 1]) ++g;
+  return g;
+}
+
+template <typename T>
+__device__ __forceinline__ T* mat_ptr(void* const* tab, char* base, int64_t m, int64_t elems) {
+  return tab ? reinterpret_cast<T*>(tab[m]) : reinterpret_cast<T*>(base) + m * elems;
+}
+template <typename T>
+__device__ __forceinline__ const T* mat_cptr(const void* const* tab, const char* base, int64_t m,
+                                             int64_t elems) {
+  return tab ? reinterpret_cast<const T*>(tab[m]) : reinterpret_cast<const T*>(base) + m * elems;
+}
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <bool BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float load(const T* p) { return bf2f(*p); }
+  static __device__ __forceinline__ T cvt(float f) { return f2bf(f); }
+  static __device__ __forceinline__ float to_f(T v) { return bf2f(v); }
+};
+template <>
+struct Elem<false> {
+  using T = float;
+  static __device__ __forceinline__ float load(const T* p) { return *p; }
+  static __device__ __forceinline__ T cvt(float f) { return f; }
+  static __device__ __forceinline__ float to_f(T v) { return v; }
+};
+
+// Sum of v over the 256-thread block, in a fixed order (deterministic).
+// `red` must hold 4 floats of LDS.  Result valid in every thread.
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_head(const Batch& bt, const Work& wk, bool bf16, float momentum, hipStream_t s);
+hipError_t launch_norm_finalize(const Batch& bt, const Work& wk, hipStream_t s);
+hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps,
+                              hipStream_t s);
+hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
+hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,
+                             bool coef, hipStream_t s);
+// Newton-Schulz products.  `iter` selects X0/X1 and the first-iteration norm
+// scaling.
+hipError_t launch_gram_bf16(const Batch& bt, const Work& wk, int iter, hipStream_t s);
+hipError_t launch_poly_bf16(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
+hipError_t launch_update_bf16(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);
+hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s);
+hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
+hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);
+
+}  // namespace muon

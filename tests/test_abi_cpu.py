@@ -1,0 +1,184 @@
+"""C ABI checks that need no GPU: exports, status codes, validation, workspace sizes.
+
+Every call here fails validation, and validation precedes the first HIP call,
+so nothing touches a device.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from muon_step_03_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+ES = {_lib.MUON_DTYPE_F32: 4, _lib.MUON_DTYPE_BF16: 2}
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmuon.so not built")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_expects():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    names = {0: "ok", 1: "invalid argument", 2: "invalid shape", 3: "unsupported dtype",
+             4: "workspace too small", 5: "HIP runtime error"}
+    for code, text in names.items():
+        assert _lib.status_string(code) == text
+    assert _lib.status_string(99) == "unknown status"
+    assert L.muon_last_hip_error() == 0
+
+
+def ws_formula(count, rows, cols, dtype):
+    """Workspace size from the layout the library documents (X0, X1, A, B,
+    head/tail partials, per-matrix scalars; 256-byte aligned regions)."""
+    tile = 128 if dtype == _lib.MUON_DTYPE_BF16 else 64
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    p, q = min(rows, cols), max(rows, cols)
+    pp, qp = -(-p // tile) * tile, -(-q // tile) * tile
+    es = ES[dtype]
+    head = (pp // 64) * (qp // 64)
+    tail = math.ceil(rows / 64) * math.ceil(cols / 64)
+    return (2 * al(count * pp * qp * es) + 2 * al(count * pp * pp * es) + al(count * head * 4)
+            + al(count * tail * 12) + al(count * 8 * 4) + 256)
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (768, 3072), (3072, 768), (100, 300), (1, 1),
+                                   (1408, 512), (2048, 5632)])
+@pytest.mark.parametrize("dtype", [_lib.MUON_DTYPE_F32, _lib.MUON_DTYPE_BF16])
+@pytest.mark.parametrize("count", [1, 7])
+def test_workspace_bytes(L, shape, dtype, count):
+    assert L.muon_workspace_bytes(count, *shape, dtype) == ws_formula(count, *shape, dtype)
+
+
+def test_workspace_bytes_invalid(L):
+    assert L.muon_workspace_bytes(1, 0, 5, 0) == 0
+    assert L.muon_workspace_bytes(1, 5, _lib.MUON_MAX_DIM + 1, 0) == 0
+    assert L.muon_workspace_bytes(-1, 5, 5, 0) == 0
+    assert L.muon_workspace_bytes(1, 5, 5, 7) == 0
+    assert L.muon_workspace_bytes(0, 5, 5, 0) == 0
+
+
+def test_workspace_bytes_grouped_is_sum(L):
+    shapes = [(3, 768, 768), (2, 768, 3072), (2, 3072, 768)]
+    arr = (_lib.MuonGroup * 3)(*[_lib.MuonGroup(c, r, k, None, None, None, 1, 2, 3)
+                                 for c, r, k in shapes])
+    got = L.muon_workspace_bytes_grouped(arr, 3, _lib.MUON_DTYPE_BF16)
+    want = sum(ws_formula(c, r, k, _lib.MUON_DTYPE_BF16) - 256 for c, r, k in shapes) + 256
+    assert got == want
+
+
+# Fake device addresses: never dereferenced, since every call below fails
+# validation first.
+W, G, M, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+OKARGS = dict(lr=0.02, mom=0.95, wd=0.1, ns=5, a=3.4445, b=-4.775, c=2.0315, variant=0)
+
+
+def call_step(L, W=W, G=G, M=M, rows=64, cols=128, dtype=0, ws=WS, wsb=1 << 30, stats=None,
+              **kw):
+    k = dict(OKARGS, **kw)
+    return L.muon_step(W, G, M, rows, cols, dtype, k["lr"], k["mom"], k["wd"], k["ns"], k["a"],
+                       k["b"], k["c"], k["variant"], ws, wsb, stats, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), 1), (dict(G=None), 1), (dict(M=None), 1),
+    (dict(rows=0), 2), (dict(cols=0), 2), (dict(rows=-3), 2),
+    (dict(cols=_lib.MUON_MAX_DIM + 1), 2),
+    (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(ns=-1), 1), (dict(ns=_lib.MUON_MAX_NS_STEPS + 1), 1),
+    (dict(lr=float("nan")), 1), (dict(mom=float("inf")), 1), (dict(wd=float("-inf")), 1),
+    (dict(a=float("nan")), 1), (dict(b=float("inf")), 1), (dict(c=float("nan")), 1),
+    (dict(variant=2), 1), (dict(variant=-1), 1),
+    (dict(ws=None), 1), (dict(wsb=1000), 4),
+    (dict(G=W), 1),                          # W and G alias
+    (dict(M=W + 64), 1),                     # M overlaps W
+    (dict(ws=G - 1024, wsb=1 << 20), 1),     # workspace overlaps G
+])
+def test_step_validation(L, kw, status):
+    assert call_step(L, **kw) == status
+
+
+def test_workspace_exact_size_boundary(L):
+    need = L.muon_workspace_bytes(1, 64, 128, 0)
+    assert call_step(L, wsb=need - 1) == _lib.MUON_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_batched_validation(L):
+    P = ctypes.c_void_p
+    args = (0, 0.02, 0.95, 0.1, 5, 3.4445, -4.775, 2.0315, 0, WS, 1 << 30, None, None)
+    assert L.muon_step_batched(None, P(G), P(M), 4, 64, 64, *args) == 1
+    assert L.muon_step_batched(P(W), P(G), P(M), -1, 64, 64, *args) == 1
+    assert L.muon_step_batched(P(W), P(G), P(M), 4, 0, 64, *args) == 2
+    # Empty batch: a no-op, no workspace needed, nothing enqueued.
+    assert L.muon_step_batched(None, None, None, 0, 64, 64, *args) == 0
+
+
+def test_grouped_validation(L):
+    args = (0, 0.02, 0.95, 0.1, 5, 3.4445, -4.775, 2.0315, 0, WS, 1 << 34, None, None)
+    def grp(**kw):
+        d = dict(count=2, rows=64, cols=64, W_table=None, G_table=None, M_table=None,
+                 W=None, G=None, M=None)
+        d.update(kw)
+        return _lib.MuonGroup(**d)
+    arr = lambda *g: (_lib.MuonGroup * len(g))(*g)  # noqa: E731
+    # neither pointer form / both forms / a partial form
+    assert L.muon_step_grouped(arr(grp()), 1, *args) == 1
+    assert L.muon_step_grouped(arr(grp(W=W, G=G, M=M, W_table=1, G_table=2, M_table=3)), 1,
+                               *args) == 1
+    assert L.muon_step_grouped(arr(grp(W_table=1, G_table=2)), 1, *args) == 1
+    assert L.muon_step_grouped(arr(grp(W=W, G=G)), 1, *args) == 1
+    # stacks that overlap: 2 x 64 x 64 floats starting 1 KiB apart
+    assert L.muon_step_grouped(arr(grp(W=W, G=W + 1024, M=M)), 1, *args) == 1
+    assert L.muon_step_grouped(None, 1, *args) == 1
+    assert L.muon_step_grouped(None, -1, *args) == 1
+    # bad shape in a later group is still caught before any work
+    good = grp(W=W, G=G, M=M)
+    assert L.muon_step_grouped(arr(good, grp(rows=0, W=W, G=G, M=M)), 2, *args) == 2
+    # empty: no groups, or only count-0 groups
+    assert L.muon_step_grouped(None, 0, *args) == 0
+    assert L.muon_step_grouped(arr(grp(count=0)), 1, *args) == 0
+    # too many blocks for one launch
+    huge = grp(count=1 << 20, rows=4096, cols=4096, W=W, G=G + (1 << 50), M=M + (1 << 52))
+    assert L.muon_step_grouped(arr(huge), 1, *args) == 2
+
+
+def test_phase_names_and_profile_args(L):
+    names = [L.muon_phase_name(i).decode() for i in range(_lib.MUON_NUM_PHASES)]
+    assert names == ["head", "norm_finalize", "gram", "poly", "update", "tail_reduce",
+                     "tail_finalize", "tail_apply"]
+    assert L.muon_phase_name(8) == b"?" and L.muon_phase_name(-1) == b"?"
+    assert L.muon_profile_read(None, None, 8) == 1
+    ms = (ctypes.c_double * 8)()
+    n = (ctypes.c_int64 * 8)()
+    assert L.muon_profile_read(ms, n, 0) == 1
+    # nothing recorded yet: reads back zeros without touching a device
+    assert L.muon_profile_read(ms, n, 8) == 0 and sum(n) == 0
+
+
+def test_python_binding_rejects_non_2d():
+    torch = pytest.importorskip("torch")
+    from muon_step_03_amd import MuonStep, muon_step
+    with pytest.raises(ValueError):
+        MuonStep([torch.nn.Parameter(torch.zeros(8))])
+    with pytest.raises(ValueError):
+        muon_step(torch.zeros(4, 4, 4), torch.zeros(4, 4, 4), torch.zeros(4, 4, 4))

@@ -80,14 +80,16 @@ def check_against_oracle(W0, G, M0, W1, M1, variant="muon", tol=None, stats=None
     return e_dw, e_m, st
 
 
-def check_bf16_within_one_ulp(W1, Wr):
-    """Every bf16 output equals the exact result rounded to bf16, or its
-    neighbour (the GPU rounds its own float32 result once)."""
+def check_bf16_elementwise(W1, Wr, slack):
+    """Every bf16 output lies within one bf16 ulp of the exact result rounded
+    to bf16, plus `slack` (per element: what the bf16 storage of the iterate
+    may move the exact result)."""
     w1 = f64(W1)
     ref = bf16_round(Wr)
     ulp = np.abs(bf16_round(np.nextafter(np.abs(ref), np.inf) * 1.0040) - np.abs(ref))
     ulp = np.maximum(ulp, 2.0 ** -133)
-    assert np.all(np.abs(w1 - ref) <= ulp * 1.0001), float(np.max(np.abs(w1 - ref) / ulp))
+    excess = np.abs(w1 - ref) - (ulp * 1.0001 + slack)
+    assert np.all(excess <= 0), float(np.max(excess))
 
 
 def recovered_update(W0, W1, lr, wd):

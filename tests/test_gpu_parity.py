@@ -15,7 +15,7 @@ import oracle
 from muon_step_03_amd import (MuonError, MuonStep, muon_step, muon_step_batched,
                               muon_step_grouped, stacked_group)
 from muon_step_03_amd import workloads as wl
-from _parity import (HP, TOL_BF16, TOL_F32, check_against_oracle, check_bf16_within_one_ulp,
+from _parity import (HP, TOL_BF16, TOL_F32, check_against_oracle, check_bf16_elementwise,
                      check_muongs_invariants, f64, oracle_step, relF)
 
 pytestmark = pytest.mark.gpu
@@ -92,7 +92,12 @@ def test_few_ns_steps(dtype, ns):
     W1, M1, st = gpu_step(W, G, M, ns_steps=ns)
     if dtype == torch.bfloat16 and ns == 0:
         Wr, Mr, _ = oracle_step(W, G, M, ns_steps=0)
-        check_bf16_within_one_ulp(W1, Wr)
+        _, U = oracle.nesterov_momentum(f64(G), f64(M), 0.95)
+        O = oracle.newton_schulz(U, *oracle.NS_COEFFICIENTS, 0)
+        step = 0.02 * 0.2 * math.sqrt(max(W.shape))
+        # X0 holds U rounded to bf16: up to 2^-9 relative per element, so
+        # lr*s*2^-8*|O| bounds what it can move W' before the final rounding.
+        check_bf16_elementwise(W1, Wr, slack=step * 2.0 ** -8 * np.abs(O))
         assert relF(f64(M1), Mr) <= 1e-6
     else:
         check_against_oracle(W, G, M, W1, M1, stats=st, ns_steps=ns)

@@ -7,9 +7,7 @@
 //                             computed, each written to both triangles
 //   B = b*A + c*A A^T         A is symmetric, so A A = A A^T: the same
 //                             symmetric form with K = p and the b*A epilogue
-//   X' = a*X + B X            full p x q output; X is N-contiguous, so its
-//                             tiles are transposed in registers on the way
-//                             into LDS
+//   X' = a*X + B X            full p x q output
 // which is X_k = aX + b(XX^T)X + c(XX^T)^2 X of "[논문 AI 리뷰] MUON IS
 // SCALABLE FOR LLM TRAINING TECHNICAL REPORT", section 2, and the three-line
 // Newton-Schulz code block of "LLM Pretraining Loss Spike 진단과 처방 ... Muon
@@ -19,11 +17,29 @@
 // ||U|| while it writes X0): its Gram is scaled by inv^2 and its update by
 // inv, inv = 1/(||U||_F + 1e-7), which is the iteration applied to U*inv.
 //
-// Block tile 128x128, K step 64, 256 threads = 4 waves in a 2x2 grid, each
-// wave a 64x64 sub-tile of 2x2 MFMA 32x32 outputs.  LDS rows hold 64 bf16
-// (128 bytes) of one operand row; 16-byte chunks are XOR-swizzled by
-// (row + row/8) mod 8 so that fragment reads (32 consecutive rows, one chunk)
-// and the transposing 8-byte writes are bank-conflict free.
+// Kernel structure (256 threads = 4 waves in a 2x2 grid):
+//  * Block tiles are compile-time (defaults: symmetric products 128x128,
+//    64x64 per wave; update 128x256, 64x128 per wave, fewer LDS reads per
+//    MFMA).
+//  * K steps of 32, staged through LDS by 16-byte direct-to-LDS loads
+//    (global_load_lds): STAGES buffers, loads for up to STAGES-1 later steps
+//    in flight while step k is multiplied; one barrier per K step, and the
+//    MFMA fragments double-buffered in registers.
+//  * K-contiguous operand tiles: rows of 32 bf16 (64 B, 4 chunks of 16 B),
+//    chunk c of row m stored at c ^ f(m), f(m) = ((m>>1) + (m>>3)) & 3,
+//    so the fragment reads (32 consecutive rows, one chunk) do not collide
+//    in 32- or 64-bank LDS.  The swizzle is applied by choosing which
+//    global chunk each lane fetches (a direct-to-LDS load writes lane L's
+//    16 bytes at base + 16 L).
+//  * The update's X operand is N-contiguous: its tile is kept as 32 K-rows
+//    of BN bf16 (chunk c of row k stored at c ^ g(k), g = {0,6,12,10}[k&3])
+//    and MFMA B fragments are read with the transposing LDS read
+//    ds_read_b64_tr_b16: within a 16-lane group, output lane i element j
+//    comes from source lane 4j + i/4, element i%4, so lane s addresses
+//    X[k0 + s/4][n0 + 4 (s%4)] and two reads give 8 consecutive k.
+//  * Blocks are renumbered so that consecutive tiles (same matrix) land on
+//    the same XCD (hardware dispatches block b to XCD b % 8), keeping one
+//    matrix's operands in one XCD's L2.
 #include "muon_internal.h"
 
 namespace muon {
@@ -31,19 +47,71 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = kBf16Tile;      // 128
-constexpr int BK = 64;
-constexpr int ROWB = BK * 2;       // bytes per LDS row
-constexpr int TILEB = BM * ROWB;   // 16 KB per operand tile
+constexpr int BK = 32;
+constexpr int CHUNK = 16;           // bytes per direct-to-LDS lane transfer
+constexpr int WAVE_BYTES = 1024;    // bytes one direct-to-LDS instruction moves
 
 enum { MODE_GRAM = 0, MODE_POLY = 1, MODE_UPDATE = 2 };
 
-__device__ __forceinline__ int swz(int row) { return (row + (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ swz(row)) << 4);
+template <int MODE>
+struct Cfg;
+#ifndef MUON_SYRK_STAGES
+#define MUON_SYRK_STAGES 4
+#endif
+#ifndef MUON_UPD_STAGES
+#define MUON_UPD_STAGES 3
+#endif
+template <>
+struct Cfg<MODE_GRAM> {
+  static constexpr int BM = kSyrkTile, BN = kSyrkTile, WM = BM / 64, WN = BN / 64;
+  static constexpr int STAGES = MUON_SYRK_STAGES;
+  static constexpr int OCC = (WM * WN >= 16) ? 1 : 2;  // blocks per CU the registers allow
+};
+template <>
+struct Cfg<MODE_POLY> : Cfg<MODE_GRAM> {};
+template <>
+struct Cfg<MODE_UPDATE> {
+  static constexpr int BM = kUpdTileM, BN = kUpdTileN, WM = BM / 64, WN = BN / 64;
+  static constexpr int STAGES = MUON_UPD_STAGES;
+  static constexpr int OCC = (WM * WN >= 16) ? 1 : 2;
+};
+
+__device__ __forceinline__ int fswz(int m) { return ((m >> 1) + (m >> 3)) & 3; }
+__device__ __forceinline__ int gswz(int k) { return (0xACE0 >> ((k & 3) * 4)) & 15; }  // {0,6,12,10}
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16-byte direct-to-LDS load: lane L's 16 bytes from `src` land at LDS
+// address lds_base + 16 L (lds_base wave-uniform, passed in m0).  Written as
+// asm so that the compiler does not treat every later LDS read as possibly
+// aliasing it (which would make it wait for all loads in flight, prefetches
+// included); completion is tracked explicitly with wait_vmcnt before the
+// barrier that publishes a K step.  The instruction has no result register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier without a memory fence (which would wait for every load
+// in flight); the empty asm keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Lower-triangle block index t -> (ti, tj), ti >= tj, row-major over ti.
@@ -55,81 +123,90 @@ __device__ __forceinline__ void tri_decode(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
-// 128 rows x 64 K-contiguous bf16 from global: thread t takes rows
-// t/8 + 32*r, 16-byte chunk t%8 (8 threads per 128-byte row segment).
-__device__ __forceinline__ void gload_rows(const uint16_t* base, int64_t ld, int k0,
-                                           u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
-  const int row = t >> 3, ch = t & 7;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = *reinterpret_cast<const u32x4_t*>(base + int64_t(row + 32 * i) * ld + k0 + ch * 8);
-}
-__device__ __forceinline__ void sstore_rows(char* lds, const u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
-  const int row = t >> 3, ch = t & 7;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(lds + lds_off(row + 32 * i, ch)) = r[i];
+// Within one group's block range (padded to a multiple of 8 and starting at a
+// multiple of 8), block j runs on XCD j % 8 (hardware round-robin); renumber
+// so that XCD x takes the contiguous tile range [x*n/8, (x+1)*n/8): every
+// XCD gets the same share of every group, and consecutive tiles (one
+// matrix's) share an XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t j, int64_t npad) {
+#ifdef MUON_NO_XCD_REMAP
+  return j;
+#endif
+  return (j & 7) * (npad >> 3) + (j >> 3);
 }
 
-// X tile of the update: 64 K-rows x 128 N-columns, N contiguous in memory.
-// Thread t loads rows k0 + 4*(t/16) + i (i = 0..3), columns 8*(t%16) .. +7.
-__device__ __forceinline__ void gload_xT(const uint16_t* base, int64_t ld, int k0,
-                                         u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
-  const int nb = t & 15, kq = t >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = *reinterpret_cast<const u32x4_t*>(base + int64_t(k0 + 4 * kq + i) * ld + nb * 8);
+// One direct-to-LDS instruction of a K-contiguous tile: 16 rows x 64 bytes.
+// Lane L takes row r0 + L/4, physical chunk L%4, i.e. logical chunk
+// (L%4) ^ f(row).
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t ld, int k0, int r0,
+                                         uint32_t tile, int lane) {
+  const int row = r0 + (lane >> 2);
+  const int c = (lane & 3) ^ fswz(row);
+  dma16(base + int64_t(row) * ld + k0 + c * 8, tile + r0 * (BK * 2));
 }
-// ... and stores it as 128 N-rows of 64 K-contiguous bf16: for each of its 8
-// columns the thread packs its 4 K values into 8 bytes.
-__device__ __forceinline__ void sstore_xT(char* lds, const u32x4_t (&r)[4]) {
-  const int t = threadIdx.x;
-  const int nb = t & 15, kq = t >> 4;
-  const int chunk = kq >> 1, sub = (kq & 1) * 8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = e >> 1;
-    uint32_t lo, hi;
-    if (e & 1) {
-      lo = (r[0][d] >> 16) | (r[1][d] & 0xffff0000u);
-      hi = (r[2][d] >> 16) | (r[3][d] & 0xffff0000u);
-    } else {
-      lo = (r[0][d] & 0xffffu) | (r[1][d] << 16);
-      hi = (r[2][d] & 0xffffu) | (r[3][d] << 16);
-    }
-    const int n = nb * 8 + e;
-    u32x2_t v;
-    v[0] = lo;
-    v[1] = hi;
-    *reinterpret_cast<u32x2_t*>(lds + lds_off(n, chunk) + sub) = v;
-  }
+
+// One direct-to-LDS instruction of the update's X tile: 1024/(2 BN) K-rows
+// of 2 BN bytes.  Lane L takes K-row kr0 + L/(BN/8), physical chunk L%(BN/8).
+template <int BN>
+__device__ __forceinline__ void dma_xrows(const uint16_t* base, int64_t ld, int k0, int kr0,
+                                          uint32_t tile, int lane) {
+  constexpr int CPR = BN / 8;  // 16-byte chunks per row
+  const int k = kr0 + lane / CPR;
+  const int c = (lane % CPR) ^ gswz(k);
+  dma16(base + int64_t(k0 + k) * ld + c * 8, tile + kr0 * (BN * 2));
+}
+
+__device__ __forceinline__ bf16x8_t lds_frag_rows(const LDS_AS char* tile, int row, int chunk) {
+  return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * (BK * 2) + ((chunk ^ fswz(row)) << 4));
+}
+
+template <int BN>
+__device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb, int nb, int lane) {
+  const int s = lane & 15;
+  const int n = nb + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int k = kb + 8 * (lane >> 5) + (s >> 2);
+  const LDS_AS char* p0 = tile + k * (BN * 2) + (((n >> 3) ^ gswz(k)) << 4) + (n & 7) * 2;
+  const LDS_AS char* p1 = tile + (k + 4) * (BN * 2) + (((n >> 3) ^ gswz(k + 4)) << 4) + (n & 7) * 2;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p1);
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void ns_bf16_kernel(Batch bt, Work wk, int iter, float c1,
-                                                         float c2) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * TILEB];
-  char* sA = lds;
-  char* sB = lds + TILEB;
+__global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, Work wk, int iter,
+                                                                     float c1, float c2) {
+  using C = Cfg<MODE>;
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES;
+  constexpr int A_BYTES = BM * BK * 2;
+  constexpr int B_BYTES = BN * BK * 2;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  constexpr int A_INSTR = A_BYTES / WAVE_BYTES / 4;  // per wave
+  constexpr int B_INSTR = B_BYTES / WAVE_BYTES / 4;
+  constexpr int LOADS = A_INSTR + B_INSTR;          // vmcnt per stage per wave
+  static_assert(A_BYTES % (4 * WAVE_BYTES) == 0 && B_BYTES % (4 * WAVE_BYTES) == 0, "tiling");
+  static_assert((S - 1) * LOADS < 64, "vmcnt field");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE_BYTES];
+  LDS_AS char* smem = (LDS_AS char*)(smem_raw);
+  (void)c2;
 
   const int64_t bid = blockIdx.x;
   const int gi = find_group(wk, bid);
   const MatGroup& g = bt.g[gi];
-  const int64_t local = bid - wk.begin[gi];
   const int tiles = wk.tiles[gi];
+  const int64_t local = xcd_remap(bid - wk.begin[gi], wk.begin[gi + 1] - wk.begin[gi]);
+  if (local >= g.count * tiles) return;  // padding block
   const int64_t m = local / tiles;
   const int tile = int(local - m * tiles);
   int ti, tj;
   if (MODE == MODE_UPDATE) {
-    const int ntn = g.q_pad / BM;
+    const int ntn = g.q_pad / BN;
     ti = tile / ntn;
     tj = tile - ti * ntn;
   } else {
     tri_decode(tile, ti, tj);
   }
-  const int i0 = ti * BM, j0 = tj * BM;
+  const int i0 = ti * BM, j0 = tj * BN;
   const int64_t qp = g.q_pad, pp = g.p_pad;
 
   const uint16_t* Xin = reinterpret_cast<const uint16_t*>((iter & 1) ? g.X1 : g.X0) + m * g.x_stride;
@@ -158,61 +235,120 @@ __global__ __launch_bounds__(256, 2) void ns_bf16_kernel(Batch bt, Work wk, int 
     ldb = qp;
     K = g.p_pad;
   }
+  const int nk = K / BK;
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
 
-  f32x16_t acc[2][2];
+  // Issue the loads of K step `kt` into stage buffer kt % S.  Each wave moves
+  // A_INSTR + B_INSTR KiB-sized pieces.
+  auto issue = [&](int kt) {
+    const uint32_t st = smem_base + uint32_t((kt % S) * STAGE_BYTES);
+    const int k0 = kt * BK;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int i = 0; i < A_INSTR; ++i) dma_rows(Pa, lda, k0, (wave * A_INSTR + i) * 16, st, lane);
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  u32x4_t ra[4], rb[4];
-  gload_rows(Pa, lda, 0, ra);
-  if (MODE == MODE_UPDATE)
-    gload_xT(Pb, ldb, 0, rb);
-  else
-    gload_rows(Pb, ldb, 0, rb);
-
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    sstore_rows(sA, ra);
-    if (MODE == MODE_UPDATE)
-      sstore_xT(sB, rb);
-    else
-      sstore_rows(sB, rb);
-    __syncthreads();
-    if (k0 + BK < K) {  // next K tile in flight while this one is multiplied
-      gload_rows(Pa, lda, k0 + BK, ra);
+    for (int i = 0; i < B_INSTR; ++i) {
       if (MODE == MODE_UPDATE)
-        gload_xT(Pb, ldb, k0 + BK, rb);
+        dma_xrows<BN>(Pb, ldb, k0, (wave * B_INSTR + i) * (1024 / (BN * 2)), st + A_BYTES, lane);
       else
-        gload_rows(Pb, ldb, k0 + BK, rb);
+        dma_rows(Pb, ldb, k0, (wave * B_INSTR + i) * 16, st + A_BYTES, lane);
     }
+  };
+
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      bf16x8_t af[2], bfr[2];
+  for (int s = 0; s < S; ++s)
+    if (s < nk) issue(s);
+
+  // MFMA 32x32 output layout: lane l, register r holds row
+  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block.
+  auto out_row = [&](int mi, int r) {
+    return i0 + wm * 32 * WM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  };
+  auto out_col = [&](int ni) { return j0 + wn * 32 * WN + ni * 32 + (lane & 31); };
+
+  // The update's a*X term starts the accumulator, and the polynomial's b*A
+  // term is fetched now, so the epilogue issues no dependent loads.
+  f32x16_t acc[WM][WN];
+  float pre[MODE == MODE_POLY ? WM : 1][MODE == MODE_POLY ? WN : 1][16];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(sA + lds_off(wm * 64 + mi * 32 + (lane & 31), ch));
+  for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(sB + lds_off(wn * 64 + ni * 32 + (lane & 31), ch));
+    for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int r = 0; r < 16; ++r) {
+        if (MODE == MODE_UPDATE) {
+          acc[mi][ni][r] = c1 * bf2f(Xin[out_row(mi, r) * qp + out_col(ni)]);
+        } else {
+          acc[mi][ni][r] = 0.f;
+          if (MODE == MODE_POLY) pre[mi][ni][r] = bf2f(Am[out_row(mi, r) * pp + out_col(ni)]);
+        }
+      }
+
+  // Fragments of one 16-deep K sub-step of stage buffer `buf`.
+  auto load_frags = [&](int buf, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
+    const LDS_AS char* sA = smem + buf * STAGE_BYTES;
+    const LDS_AS char* sB = sA + A_BYTES;
+    const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    for (int mi = 0; mi < WM; ++mi) af[mi] = lds_frag_rows(sA, wm * 32 * WM + mi * 32 + (lane & 31), ch);
+#pragma unroll
+    for (int ni = 0; ni < WN; ++ni) {
+      if (MODE == MODE_UPDATE)
+        bfr[ni] = lds_frag_xT<BN>(sB, ks * 16, wn * 32 * WN + ni * 32, lane);
+      else
+        bfr[ni] = lds_frag_rows(sB, wn * 32 * WN + ni * 32 + (lane & 31), ch);
     }
-    __syncthreads();
+  };
+  auto mfmas = [&](const bf16x8_t (&af)[WM], const bf16x8_t (&bfr)[WN]) {
+#pragma unroll
+    for (int mi = 0; mi < WM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < WN; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+  };
+  // Waits until the loads of `stage` are done: the loads of the stages
+  // issued after it (at most min(S-1, nk-1-stage) of them) may stay in flight.
+  auto wait_stage = [&](int stage) {
+    const int younger = nk - 1 - stage;
+    if (younger >= S - 1)
+      wait_vmcnt<(S - 1) * LOADS>();
+    else if (S > 3 && younger == 2)
+      wait_vmcnt<2 * LOADS>();
+    else if (younger == 1)
+      wait_vmcnt<LOADS>();
+    else
+      wait_vmcnt<0>();
+  };
+
+  // Software pipeline over K steps (two 16-deep sub-steps each): the LDS
+  // reads of the next sub-step are always in flight while the MFMAs of the
+  // current one issue.  One barrier per K step, between its sub-steps: all
+  // reads of step kt are complete there (lgkmcnt 0), so its buffer is
+  // refilled with step kt+S right after it, and step kt+1 (waited for by
+  // every wave) becomes readable.
+  bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
+  wait_stage(0);
+  block_barrier();
+  load_frags(0, 0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % S;
+    load_frags(buf, 1, a1, b1);
+    mfmas(a0, b0);
+    if (kt + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));  // lgkmcnt(0)
+      wait_stage(kt + 1);
+      block_barrier();
+      if (kt + S < nk) issue(kt + S);
+      load_frags((kt + 1) % S, 0, a0, b0);
+    }
+    mfmas(a1, b1);
   }
 
-  // Epilogue.  MFMA 32x32 output layout: lane l, register r holds row
-  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 block.
+  // Epilogue.
   const float* sc = g.scal + m * kScal;
   float alpha = 1.f, beta = 0.f;
   if (MODE == MODE_GRAM) {
@@ -226,25 +362,24 @@ __global__ __launch_bounds__(256, 2) void ns_bf16_kernel(Batch bt, Work wk, int 
   }
   const bool mirror = (MODE != MODE_UPDATE) && (ti != tj);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = j0 + wn * 64 + ni * 32 + (lane & 31);
-        float v = acc[mi][ni][r];
+        const int row = out_row(mi, r);
+        const int col = out_col(ni);
+        const float v = acc[mi][ni][r];
         if (MODE == MODE_GRAM) {
           const uint16_t h = f2bf(alpha * v);
           Am[row * pp + col] = h;
           if (mirror) Am[col * pp + row] = h;
         } else if (MODE == MODE_POLY) {
-          const uint16_t h = f2bf(fmaf(alpha, v, beta * bf2f(Am[row * pp + col])));
+          const uint16_t h = f2bf(fmaf(alpha, v, beta * pre[mi][ni][r]));
           Bm[row * pp + col] = h;
           if (mirror) Bm[col * pp + row] = h;
         } else {
-          const float x = bf2f(Xin[row * qp + col]);
-          Xout[row * qp + col] = f2bf(alpha * fmaf(c1, x, v));
+          Xout[row * qp + col] = f2bf(alpha * v);
         }
       }
 }

@@ -51,7 +51,8 @@ struct Layout {
   int64_t p, q, p_pad, q_pad;
   int trans;
   int64_t head_tiles, tail_tiles, tail_tiles_c;
-  int64_t tile;             // NS GEMM block tile edge
+  int64_t tile;             // NS GEMM block tile edge along p
+  int64_t tile_n;           // update GEMM block tile edge along q
   size_t x_bytes, a_bytes, head_bytes, tail_bytes, scal_bytes;
   size_t total;             // 0 on overflow
 };
@@ -59,12 +60,13 @@ struct Layout {
 Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
   Layout L{};
   const size_t es = dtype == MUON_DTYPE_BF16 ? 2 : 4;
-  L.tile = dtype == MUON_DTYPE_BF16 ? kBf16Tile : kF32Tile;
+  L.tile = dtype == MUON_DTYPE_BF16 ? kBf16PadP : kF32Tile;
   L.trans = rows > cols ? 1 : 0;
   L.p = rows < cols ? rows : cols;
   L.q = rows < cols ? cols : rows;
+  L.tile_n = dtype == MUON_DTYPE_BF16 ? kBf16PadQ : kF32Tile;
   L.p_pad = round_up(L.p, L.tile);
-  L.q_pad = round_up(L.q, L.tile);
+  L.q_pad = round_up(L.q, L.tile_n);
   L.head_tiles = (L.p_pad / kEwTile) * (L.q_pad / kEwTile);
   L.tail_tiles_c = cdiv(cols, kEwTile);
   L.tail_tiles = cdiv(rows, kEwTile) * L.tail_tiles_c;
@@ -125,12 +127,13 @@ int check_group(const muon_group& g, int dtype) {
 struct PhaseTiles {
   int64_t head, gram, update, tail;
 };
-PhaseTiles phase_tiles(const Layout& L) {
+PhaseTiles phase_tiles(const Layout& L, bool bf16) {
   PhaseTiles t;
-  const int64_t nt = L.p_pad / L.tile;
+  const int64_t ts = bf16 ? kSyrkTile : kF32Tile;
+  const int64_t nt = L.p_pad / ts;
   t.head = L.head_tiles;
   t.gram = nt * (nt + 1) / 2;
-  t.update = nt * (L.q_pad / L.tile);
+  t.update = bf16 ? (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN) : nt * (L.q_pad / kF32Tile);
   t.tail = L.tail_tiles;
   return t;
 }
@@ -218,7 +221,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     if (groups[i].count == 0) continue;
     const Layout L = make_layout(groups[i].count, groups[i].rows, groups[i].cols, dtype);
     if (L.total == 0) return MUON_ERR_INVALID_SHAPE;
-    const PhaseTiles pt = phase_tiles(L);
+    const PhaseTiles pt = phase_tiles(L, dtype == MUON_DTYPE_BF16);
     int64_t most = pt.head > pt.update ? pt.head : pt.update;
     most = most > pt.tail ? most : pt.tail;
     // The dispatch grid is counted in work-items (32 bits): at 256 threads a
@@ -322,7 +325,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       m.decay = float(1.0 - lr * wd);
       m.step = float(lr * 0.2 * std::sqrt(double(L.q)));
 
-      const PhaseTiles pt = phase_tiles(L);
+      const PhaseTiles pt = phase_tiles(L, dtype == MUON_DTYPE_BF16);
       w_head.tiles[k] = int(pt.head);
       w_one.tiles[k] = 1;
       w_gram.tiles[k] = int(pt.gram);
@@ -332,8 +335,12 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     hipEvent_t t0 = nullptr;
     Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};
     for (Work* w : ws) {
+      // The Newton-Schulz launches pad each group's block range to a
+      // multiple of 8 (one block per XCD slot); padding blocks exit at once.
+      const int64_t pad = (w == &w_gram || w == &w_upd) && bf16 ? 8 : 1;
       w->begin[0] = 0;
-      for (int k = 0; k < nsel; ++k) w->begin[k + 1] = w->begin[k] + bt.g[k].count * w->tiles[k];
+      for (int k = 0; k < nsel; ++k)
+        w->begin[k + 1] = w->begin[k] + (bt.g[k].count * w->tiles[k] + pad - 1) / pad * pad;
     }
 
     if ((t0 = prof_start(s)), (st = finish_launch(launch_head(bt, w_head, bf16, h.momentum, s), 0, s, t0))) return st;

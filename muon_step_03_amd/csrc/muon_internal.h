@@ -1,7 +1,9 @@
 // Internal structures shared by the host dispatcher and the HIP kernels.
 //
 // Data layout in HBM (per shape group; every region 256-byte aligned):
-//   X0, X1  [count][p_pad][q_pad]   Newton-Schulz iterate, ping-pong.  X is
+//   X0, X1  [count][p_pad][q_pad]   Newton-Schulz iterate, ping-pong
+//                                   (p_pad, q_pad: multiples of the GEMM
+//                                   block tiles).  X is
 //                                   the momentum look-ahead U in "short side
 //                                   first" orientation: X = U if rows <= cols,
 //                                   X = U^T otherwise.  Rows/cols beyond p/q
@@ -25,7 +27,22 @@ namespace muon {
 
 constexpr int kMaxGroups = MUON_GROUPS_PER_LAUNCH;
 constexpr int kEwTile = 64;        // head/tail tile edge (elements)
-constexpr int kBf16Tile = 128;     // bf16 MFMA GEMM block tile edge
+// bf16 Newton-Schulz block tiles (wave tile = block tile / 2 in each
+// dimension, 4 waves per block).
+#ifndef MUON_SYRK_TILE
+#define MUON_SYRK_TILE 128
+#endif
+#ifndef MUON_UPD_TILE_M
+#define MUON_UPD_TILE_M 128
+#endif
+#ifndef MUON_UPD_TILE_N
+#define MUON_UPD_TILE_N 256
+#endif
+constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
+constexpr int kUpdTileM = MUON_UPD_TILE_M;  // update: rows (along p)
+constexpr int kUpdTileN = MUON_UPD_TILE_N;  // update: columns (along q)
+constexpr int kBf16PadP = kSyrkTile > kUpdTileM ? kSyrkTile : kUpdTileM;
+constexpr int kBf16PadQ = kUpdTileN > kSyrkTile ? kUpdTileN : kSyrkTile;
 constexpr int kF32Tile = 64;       // fp32 GEMM block tile edge
 constexpr float kEps = 1e-7f;      // added to ||U||_F before dividing
 

@@ -51,10 +51,10 @@ def test_status_strings(L):
 def ws_formula(count, rows, cols, dtype):
     """Workspace size from the layout the library documents (X0, X1, A, B,
     head/tail partials, per-matrix scalars; 256-byte aligned regions)."""
-    tile = 128 if dtype == _lib.MUON_DTYPE_BF16 else 64
+    tile_p, tile_q = (128, 256) if dtype == _lib.MUON_DTYPE_BF16 else (64, 64)
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     p, q = min(rows, cols), max(rows, cols)
-    pp, qp = -(-p // tile) * tile, -(-q // tile) * tile
+    pp, qp = -(-p // tile_p) * tile_p, -(-q // tile_q) * tile_q
     es = ES[dtype]
     head = (pp // 64) * (qp // 64)
     tail = math.ceil(rows / 64) * math.ceil(cols / 64)

@@ -47,12 +47,12 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BK = 32;
-constexpr int CHUNK = 16;           // bytes per direct-to-LDS lane transfer
 constexpr int WAVE_BYTES = 1024;    // bytes one direct-to-LDS instruction moves
 
 enum { MODE_GRAM = 0, MODE_POLY = 1, MODE_UPDATE = 2 };
@@ -106,10 +106,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
-// Workgroup barrier without a memory fence (which would wait for every load
-// in flight); the empty asm keeps the compiler from moving LDS accesses
-// across it.
+// Workgroup barrier that publishes this wave's LDS traffic (lgkmcnt(0): its
+// LDS reads and writes are complete) but leaves global loads in flight (no
+// vmcnt wait, unlike a fence); the empty asm statements keep the compiler
+// from moving LDS accesses across it in either direction.
 __device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -171,6 +174,35 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p1);
   const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Epilogue arithmetic on 8 consecutive outputs: v = staged accumulators,
+// in = the 8 bf16 of the a*X (update) or b*A (polynomial) term.
+template <int MODE>
+__device__ __forceinline__ uint4 finish8(const float (&v)[8], uint4 in, float alpha, float c1,
+                                         float c2) {
+  const uint32_t iw[4] = {in.x, in.y, in.z, in.w};
+  uint32_t ow[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    float o0, o1;
+    if (MODE == MODE_GRAM) {
+      o0 = alpha * v[e];
+      o1 = alpha * v[e + 1];
+    } else {
+      const float x0 = __uint_as_float(iw[e >> 1] << 16);
+      const float x1 = __uint_as_float(iw[e >> 1] & 0xffff0000u);
+      if (MODE == MODE_POLY) {  // B = c (A A) + b A
+        o0 = fmaf(c2, v[e], c1 * x0);
+        o1 = fmaf(c2, v[e + 1], c1 * x1);
+      } else {                  // X' = alpha (a X + B X)
+        o0 = alpha * fmaf(c1, x0, v[e]);
+        o1 = alpha * fmaf(c1, x1, v[e + 1]);
+      }
+    }
+    ow[e >> 1] = uint32_t(f2bf(o0)) | (uint32_t(f2bf(o1)) << 16);
+  }
+  return make_uint4(ow[0], ow[1], ow[2], ow[3]);
 }
 
 template <int MODE>
@@ -263,30 +295,13 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
   for (int s = 0; s < S; ++s)
     if (s < nk) issue(s);
 
-  // MFMA 32x32 output layout: lane l, register r holds row
-  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block.
-  auto out_row = [&](int mi, int r) {
-    return i0 + wm * 32 * WM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-  };
-  auto out_col = [&](int ni) { return j0 + wn * 32 * WN + ni * 32 + (lane & 31); };
-
-  // The update's a*X term starts the accumulator, and the polynomial's b*A
-  // term is fetched now, so the epilogue issues no dependent loads.
   f32x16_t acc[WM][WN];
-  float pre[MODE == MODE_POLY ? WM : 1][MODE == MODE_POLY ? WN : 1][16];
 #pragma unroll
   for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MODE == MODE_UPDATE) {
-          acc[mi][ni][r] = c1 * bf2f(Xin[out_row(mi, r) * qp + out_col(ni)]);
-        } else {
-          acc[mi][ni][r] = 0.f;
-          if (MODE == MODE_POLY) pre[mi][ni][r] = bf2f(Am[out_row(mi, r) * pp + out_col(ni)]);
-        }
-      }
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
   // Fragments of one 16-deep K sub-step of stage buffer `buf`.
   auto load_frags = [&](int buf, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
@@ -310,19 +325,21 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
       for (int ni = 0; ni < WN; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
   };
-  // Waits until the loads of `stage` are done: the loads of the stages
-  // issued after it (at most min(S-1, nk-1-stage) of them) may stay in flight.
-  auto wait_stage = [&](int stage) {
-    const int younger = nk - 1 - stage;
-    if (younger >= S - 1)
-      wait_vmcnt<(S - 1) * LOADS>();
-    else if (S > 3 && younger == 2)
+  // Waits until the loads of `stage` are done, given that the last stage
+  // issued so far is `issued` (capped at nk-1): exactly the loads of the
+  // stages issued after `stage` may stay in flight (vmcnt counts in order).
+  auto wait_stage = [&](int stage, int issued) {
+    const int younger = (issued < nk - 1 ? issued : nk - 1) - stage;
+    if (S > 3 && younger >= 3)
+      wait_vmcnt<(S > 3 ? 3 : 0) * LOADS>();
+    else if (younger == 2)
       wait_vmcnt<2 * LOADS>();
     else if (younger == 1)
       wait_vmcnt<LOADS>();
     else
       wait_vmcnt<0>();
   };
+  static_assert(S <= 4, "wait_stage covers at most 3 younger stages");
 
   // Software pipeline over K steps (two 16-deep sub-steps each): the LDS
   // reads of the next sub-step are always in flight while the MFMAs of the
@@ -331,7 +348,7 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
   // refilled with step kt+S right after it, and step kt+1 (waited for by
   // every wave) becomes readable.
   bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
-  wait_stage(0);
+  wait_stage(0, S - 1);  // the prologue issued steps 0 .. S-1
   block_barrier();
   load_frags(0, 0, a0, b0);
   for (int kt = 0; kt < nk; ++kt) {
@@ -339,8 +356,7 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     load_frags(buf, 1, a1, b1);
     mfmas(a0, b0);
     if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));  // lgkmcnt(0)
-      wait_stage(kt + 1);
+      wait_stage(kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
       block_barrier();
       if (kt + S < nk) issue(kt + S);
       load_frags((kt + 1) % S, 0, a0, b0);
@@ -348,40 +364,87 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     mfmas(a1, b1);
   }
 
-  // Epilogue.
+  // ---- Epilogue: the fp32 accumulator tile is staged through LDS in two
+  // passes of 64 rows, so that every global access below is a 16-byte
+  // vector: the a*X term (update) and b*A term (polynomial) are read as
+  // 8-element chunks and results stored as 8-element chunks.  The mirrored
+  // half of an off-diagonal symmetric tile is produced from the same staged
+  // values read column-wise; since A is stored exactly symmetric, those are
+  // bit-identical to the values written above the diagonal.
   const float* sc = g.scal + m * kScal;
-  float alpha = 1.f, beta = 0.f;
+  float alpha = 1.f;
   if (MODE == MODE_GRAM) {
     const float inv = iter == 0 ? sc[SC_INV] : 1.f;
     alpha = inv * inv;
-  } else if (MODE == MODE_POLY) {
-    alpha = c2;  // c
-    beta = c1;   // b
-  } else {
+  } else if (MODE == MODE_UPDATE) {
     alpha = iter == 0 ? sc[SC_INV] : 1.f;
   }
   const bool mirror = (MODE != MODE_UPDATE) && (ti != tj);
+  constexpr int TP = BN + 8;                 // fp32 staging row pitch (floats)
+  static_assert(64 * TP * 4 <= S * STAGE_BYTES, "staging");
+  LDS_AS float* T = (LDS_AS float*)smem;
+  constexpr int CPR = BN / 8;                // 8-element chunks per row
+  constexpr int CHUNKS = 64 * CPR / 256;     // per thread per pass
+  block_barrier();                            // stage buffers no longer read
 #pragma unroll
-  for (int mi = 0; mi < WM; ++mi)
+  for (int pass = 0; pass < 2; ++pass) {
+    if (wm == pass) {
+      // MFMA 32x32 output layout: lane l, register r holds row
+      // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block.
 #pragma unroll
-    for (int ni = 0; ni < WN; ++ni)
+      for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = out_row(mi, r);
-        const int col = out_col(ni);
-        const float v = acc[mi][ni][r];
-        if (MODE == MODE_GRAM) {
-          const uint16_t h = f2bf(alpha * v);
-          Am[row * pp + col] = h;
-          if (mirror) Am[col * pp + row] = h;
-        } else if (MODE == MODE_POLY) {
-          const uint16_t h = f2bf(fmaf(alpha, v, beta * pre[mi][ni][r]));
-          Bm[row * pp + col] = h;
-          if (mirror) Bm[col * pp + row] = h;
-        } else {
-          Xout[row * qp + col] = f2bf(alpha * v);
-        }
+        for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int col = wn * 32 * WN + ni * 32 + (lane & 31);
+            T[row * TP + col] = acc[mi][ni][r];
+          }
+    }
+    block_barrier();
+#pragma unroll 2
+    for (int u = 0; u < CHUNKS; ++u) {
+      const int q = t + 256 * u;
+      const int row = q / CPR, col = (q % CPR) * 8;
+      const int64_t grow = i0 + 64 * pass + row, gcol = j0 + col;
+      float v[8];
+      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
+      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = v0[e];
+        v[e + 4] = v1[e];
       }
+      uint4 in = make_uint4(0, 0, 0, 0);
+      if (MODE == MODE_UPDATE) in = *reinterpret_cast<const uint4*>(Xin + grow * qp + gcol);
+      if (MODE == MODE_POLY) in = *reinterpret_cast<const uint4*>(Am + grow * pp + gcol);
+      const uint4 out = finish8<MODE>(v, in, alpha, c1, c2);
+      if (MODE == MODE_UPDATE)
+        *reinterpret_cast<uint4*>(Xout + grow * qp + gcol) = out;
+      else
+        *reinterpret_cast<uint4*>((MODE == MODE_GRAM ? Am : Bm) + grow * pp + gcol) = out;
+    }
+    if (mirror) {
+      // Mirrored block: rows j0 + c of C (c < BN), columns i0 + 64*pass + r8
+      // .. +7, from staged column c; lanes take consecutive c, so the
+      // column reads hit distinct banks.
+      uint16_t* C = MODE == MODE_GRAM ? Am : Bm;
+#pragma unroll 2
+      for (int u = 0; u < BN * 8 / 256; ++u) {
+        const int q = t + 256 * u;
+        const int c = q % BN, r8 = (q / BN) * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
+        const int64_t grow = j0 + c, gcol = i0 + 64 * pass + r8;
+        uint4 in = make_uint4(0, 0, 0, 0);
+        if (MODE == MODE_POLY) in = *reinterpret_cast<const uint4*>(Am + grow * pp + gcol);
+        *reinterpret_cast<uint4*>(C + grow * pp + gcol) = finish8<MODE>(v, in, alpha, c1, c2);
+      }
+    }
+    block_barrier();  // T is rewritten by the next pass
+  }
 }
 
 inline dim3 grid_of(const Work& wk) { return dim3(unsigned(wk.begin[wk.ngroups])); }

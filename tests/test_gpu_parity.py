@@ -207,6 +207,29 @@ def test_transpose_equivariance(dtype):
     assert relF(f64(W2).T - f64(W), f64(W1) - f64(W)) <= tol
 
 
+@pytest.mark.parametrize("variant", ["muon", "muongs"])
+def test_workspace_contents_do_not_matter(variant):
+    """The step must not read workspace it has not written: a zeroed and a
+    NaN-filled workspace (0xFF bytes) give bitwise identical results on the
+    full grouped GPT-160M launch.  Catches pipeline races that read an LDS
+    stage before its load landed, or a tile left unwritten."""
+    from muon_step_03_amd import workspace_bytes_grouped
+    w = wl.WORKLOADS["gpt160m"]
+    Gs = wl.make_grads(w, 0, DEV)
+    outs = []
+    for fill in (0x00, 0xFF):
+        Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
+        groups = [stacked_group(Ws[i], Gs[i], Ms[i]) for i in range(len(w.groups))]
+        ws = torch.full((workspace_bytes_grouped(groups, torch.bfloat16),), fill,
+                        dtype=torch.uint8, device=DEV)
+        muon_step_grouped(groups, torch.bfloat16, variant=variant, workspace=ws, **HP)
+        torch.cuda.synchronize()
+        outs.append((Ws, Ms))
+    for (Wa, Ma), (Wb, Mb) in zip(zip(*outs[0]), zip(*outs[1])):
+        assert torch.isfinite(Wa.float()).all()
+        assert torch.equal(Wa, Wb) and torch.equal(Ma, Mb)
+
+
 # ------------------------------------------- full-size workloads, sampled
 def run_workload(w, step, Ws, Ms, variant, stats=None):
     Gs = wl.make_grads(w, step, DEV)

@@ -54,8 +54,8 @@ struct Vec4<true> {  // 4 bf16 = 8 bytes
   }
   static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
     uint2 d;
-    d.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
-    d.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+    d.x = f2bf2(v[0], v[1]);
+    d.y = f2bf2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p) = d;
   }
 };

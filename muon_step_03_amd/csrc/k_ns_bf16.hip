@@ -65,11 +65,17 @@ struct Cfg;
 #ifndef MUON_UPD_STAGES
 #define MUON_UPD_STAGES 3
 #endif
+#ifndef MUON_SYRK_OCC
+#define MUON_SYRK_OCC 2
+#endif
+#ifndef MUON_UPD_OCC
+#define MUON_UPD_OCC 2
+#endif
 template <>
 struct Cfg<MODE_GRAM> {
   static constexpr int BM = kSyrkTile, BN = kSyrkTile, WM = BM / 64, WN = BN / 64;
   static constexpr int STAGES = MUON_SYRK_STAGES;
-  static constexpr int OCC = (WM * WN >= 16) ? 1 : 2;  // blocks per CU the registers allow
+  static constexpr int OCC = MUON_SYRK_OCC;  // blocks per CU the register budget targets
 };
 template <>
 struct Cfg<MODE_POLY> : Cfg<MODE_GRAM> {};
@@ -77,7 +83,7 @@ template <>
 struct Cfg<MODE_UPDATE> {
   static constexpr int BM = kUpdTileM, BN = kUpdTileN, WM = BM / 64, WN = BN / 64;
   static constexpr int STAGES = MUON_UPD_STAGES;
-  static constexpr int OCC = (WM * WN >= 16) ? 1 : 2;
+  static constexpr int OCC = MUON_UPD_OCC;
 };
 
 __device__ __forceinline__ int fswz(int m) { return ((m >> 1) + (m >> 3)) & 3; }
@@ -163,6 +169,26 @@ __device__ __forceinline__ bf16x8_t lds_frag_rows(const LDS_AS char* tile, int r
   return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * (BK * 2) + ((chunk ^ fswz(row)) << 4));
 }
 
+// Four consecutive K-rows at one column of the update's X tile, in the
+// MFMA accumulator's row pattern: lane l (s = l % 16) gets
+// X[kb + 4 (l/32) + j][nb + 16 ((l/16) % 2) + s], j = 0..3 (one transposing
+// read; source lane s addresses X[k + s/4][n + 4 (s%4)]).
+template <int BN>
+__device__ __forceinline__ i16x4_t lds_rows4_xT(const LDS_AS char* tile, int kb, int nb, int lane) {
+  const int s = lane & 15;
+  const int n = nb + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int k = kb + 4 * (lane >> 5) + (s >> 2);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_AS i16x4_t*)(tile + k * (BN * 2) + (((n >> 3) ^ gswz(k)) << 4) + (n & 7) * 2));
+}
+
+// Four consecutive K values (kb + 4 (l/32) .. +3) of row `row` of a
+// K-contiguous tile: one 8-byte read.
+__device__ __forceinline__ i16x4_t lds_k4_rows(const LDS_AS char* tile, int row, int kb, int lane) {
+  const int k = kb + 4 * (lane >> 5);
+  return *(const LDS_AS i16x4_t*)(tile + row * (BK * 2) + (((k >> 3) ^ fswz(row)) << 4) + (k & 7) * 2);
+}
+
 template <int BN>
 __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb, int nb, int lane) {
   const int s = lane & 15;
@@ -174,35 +200,6 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p1);
   const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// Epilogue arithmetic on 8 consecutive outputs: v = staged accumulators,
-// in = the 8 bf16 of the a*X (update) or b*A (polynomial) term.
-template <int MODE>
-__device__ __forceinline__ uint4 finish8(const float (&v)[8], uint4 in, float alpha, float c1,
-                                         float c2) {
-  const uint32_t iw[4] = {in.x, in.y, in.z, in.w};
-  uint32_t ow[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    float o0, o1;
-    if (MODE == MODE_GRAM) {
-      o0 = alpha * v[e];
-      o1 = alpha * v[e + 1];
-    } else {
-      const float x0 = __uint_as_float(iw[e >> 1] << 16);
-      const float x1 = __uint_as_float(iw[e >> 1] & 0xffff0000u);
-      if (MODE == MODE_POLY) {  // B = c (A A) + b A
-        o0 = fmaf(c2, v[e], c1 * x0);
-        o1 = fmaf(c2, v[e + 1], c1 * x1);
-      } else {                  // X' = alpha (a X + B X)
-        o0 = alpha * fmaf(c1, x0, v[e]);
-        o1 = alpha * fmaf(c1, x1, v[e + 1]);
-      }
-    }
-    ow[e >> 1] = uint32_t(f2bf(o0)) | (uint32_t(f2bf(o1)) << 16);
-  }
-  return make_uint4(ow[0], ow[1], ow[2], ow[3]);
 }
 
 template <int MODE>
@@ -296,12 +293,47 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     if (s < nk) issue(s);
 
   f32x16_t acc[WM][WN];
+  float pre[MODE == MODE_POLY ? WM : 1][MODE == MODE_POLY ? WN : 1][16];  // b*A term
 #pragma unroll
   for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  // The a*X term of the update and the b*A term of the polynomial need the
+  // tile's own rows i0 .. i0+127 of X (resp. A, symmetric: A[i][j] =
+  // A[j][i]); those rows pass through LDS as the B operand's K rows of K
+  // steps i0/32 .. i0/32+3.  While K step kt is resident, the wave picks up
+  // the values for its accumulator rows 32 (2 wm + mi) .. +31 when
+  // kt == i0/32 + 2 wm + mi, so the epilogue reads nothing from memory.
+  auto pick_diag = [&](int kt, const LDS_AS char* sB) {
+    if (MODE == MODE_GRAM) return;
+    const int mi = kt - i0 / BK - 2 * wm;
+    if (mi < 0 || mi >= WM) return;
+#pragma unroll
+    for (int m2 = 0; m2 < WM; ++m2) {
+      if (m2 != mi) continue;
+#pragma unroll
+      for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          i16x4_t v;
+          if (MODE == MODE_UPDATE)
+            v = lds_rows4_xT<BN>(sB, 8 * g4, wn * 32 * WN + ni * 32, lane);
+          else
+            v = lds_k4_rows(sB, wn * 32 * WN + ni * 32 + (lane & 31), 8 * g4, lane);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = __uint_as_float(uint32_t(uint16_t(v[j])) << 16);
+            if (MODE == MODE_UPDATE)
+              acc[m2][ni][4 * g4 + j] = fmaf(c1, x, acc[m2][ni][4 * g4 + j]);
+            else
+              pre[m2][ni][4 * g4 + j] = x;
+          }
+        }
+    }
+  };
 
   // Fragments of one 16-deep K sub-step of stage buffer `buf`.
   auto load_frags = [&](int buf, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
@@ -355,6 +387,7 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     const int buf = kt % S;
     load_frags(buf, 1, a1, b1);
     mfmas(a0, b0);
+    pick_diag(kt, smem + buf * STAGE_BYTES + A_BYTES);
     if (kt + 1 < nk) {
       wait_stage(kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
       block_barrier();
@@ -364,13 +397,10 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     mfmas(a1, b1);
   }
 
-  // ---- Epilogue: the fp32 accumulator tile is staged through LDS in two
-  // passes of 64 rows, so that every global access below is a 16-byte
-  // vector: the a*X term (update) and b*A term (polynomial) are read as
-  // 8-element chunks and results stored as 8-element chunks.  The mirrored
-  // half of an off-diagonal symmetric tile is produced from the same staged
-  // values read column-wise; since A is stored exactly symmetric, those are
-  // bit-identical to the values written above the diagonal.
+  // ---- Epilogue: the final fp32 tile is staged through LDS in two passes
+  // of 64 rows and stored as 16-byte vectors of 8 bf16.  The mirrored half
+  // of an off-diagonal symmetric tile is written from the same staged
+  // values read column-wise, so both halves hold identical bits.
   const float* sc = g.scal + m * kScal;
   float alpha = 1.f;
   if (MODE == MODE_GRAM) {
@@ -380,14 +410,28 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     alpha = iter == 0 ? sc[SC_INV] : 1.f;
   }
   const bool mirror = (MODE != MODE_UPDATE) && (ti != tj);
+  // Final values in fp32, before one rounding: Gram alpha*(X X^T),
+  // polynomial c*(A A) + b*A, update alpha*(a*X + B X).
+#pragma unroll
+  for (int mi = 0; mi < WM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (MODE == MODE_POLY)
+          acc[mi][ni][r] = fmaf(c2, acc[mi][ni][r], c1 * pre[mi][ni][r]);
+        else
+          acc[mi][ni][r] *= alpha;
+      }
   constexpr int TP = BN + 8;                 // fp32 staging row pitch (floats)
   static_assert(64 * TP * 4 <= S * STAGE_BYTES, "staging");
   LDS_AS float* T = (LDS_AS float*)smem;
   constexpr int CPR = BN / 8;                // 8-element chunks per row
   constexpr int CHUNKS = 64 * CPR / 256;     // per thread per pass
-  block_barrier();                            // stage buffers no longer read
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  uint16_t* Cout = MODE == MODE_UPDATE ? Xout : (MODE == MODE_GRAM ? Am : Bm);
+  const int64_t ldc = MODE == MODE_UPDATE ? qp : pp;
+
+  auto stage = [&](int pass) {
     if (wm == pass) {
       // MFMA 32x32 output layout: lane l, register r holds row
       // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block.
@@ -402,12 +446,18 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
             T[row * TP + col] = acc[mi][ni][r];
           }
     }
-    block_barrier();
-#pragma unroll 2
+  };
+  auto pack8 = [](const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = f2bf2(v[2 * e], v[2 * e + 1]);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  auto finish = [&](int pass) {
+#pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int q = t + 256 * u;
       const int row = q / CPR, col = (q % CPR) * 8;
-      const int64_t grow = i0 + 64 * pass + row, gcol = j0 + col;
       float v[8];
       const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
       const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
@@ -416,35 +466,32 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
         v[e] = v0[e];
         v[e + 4] = v1[e];
       }
-      uint4 in = make_uint4(0, 0, 0, 0);
-      if (MODE == MODE_UPDATE) in = *reinterpret_cast<const uint4*>(Xin + grow * qp + gcol);
-      if (MODE == MODE_POLY) in = *reinterpret_cast<const uint4*>(Am + grow * pp + gcol);
-      const uint4 out = finish8<MODE>(v, in, alpha, c1, c2);
-      if (MODE == MODE_UPDATE)
-        *reinterpret_cast<uint4*>(Xout + grow * qp + gcol) = out;
-      else
-        *reinterpret_cast<uint4*>((MODE == MODE_GRAM ? Am : Bm) + grow * pp + gcol) = out;
+      *reinterpret_cast<uint4*>(Cout + (i0 + 64 * pass + row) * ldc + j0 + col) = pack8(v);
     }
     if (mirror) {
       // Mirrored block: rows j0 + c of C (c < BN), columns i0 + 64*pass + r8
       // .. +7, from staged column c; lanes take consecutive c, so the
       // column reads hit distinct banks.
-      uint16_t* C = MODE == MODE_GRAM ? Am : Bm;
-#pragma unroll 2
+#pragma unroll
       for (int u = 0; u < BN * 8 / 256; ++u) {
         const int q = t + 256 * u;
         const int c = q % BN, r8 = (q / BN) * 8;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
-        const int64_t grow = j0 + c, gcol = i0 + 64 * pass + r8;
-        uint4 in = make_uint4(0, 0, 0, 0);
-        if (MODE == MODE_POLY) in = *reinterpret_cast<const uint4*>(Am + grow * pp + gcol);
-        *reinterpret_cast<uint4*>(C + grow * pp + gcol) = finish8<MODE>(v, in, alpha, c1, c2);
+        *reinterpret_cast<uint4*>(Cout + (j0 + c) * ldc + i0 + 64 * pass + r8) = pack8(v);
       }
     }
-    block_barrier();  // T is rewritten by the next pass
-  }
+  };
+
+  block_barrier();  // stage buffers no longer read
+  stage(0);
+  block_barrier();
+  finish(0);
+  block_barrier();  // T is rewritten by the next pass
+  stage(1);
+  block_barrier();
+  finish(1);
 }
 
 inline dim3 grid_of(const Work& wk) { return dim3(unsigned(wk.begin[wk.ngroups])); }

@@ -128,12 +128,14 @@ __device__ __forceinline__ const T* mat_cptr(const void* const* tab, const char*
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// float -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// float -> bf16, round to nearest even (the hardware conversion
+// v_cvt_pk_bf16_f32); NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two floats -> two bf16 packed in one word (a in the low half), one instruction.
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <bool BF16>

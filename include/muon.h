@@ -46,8 +46,9 @@
  *           on entry are ignored and are garbage on exit.
  *  Stats    optional device float array, MUON_STATS_PER_MATRIX floats per
  *           matrix (matrix order: group by group, then index within the
- *           group): ||U||_F, ||W||_F^2, <W,O>_F, ||O||_F^2, ||O~||_F^2, all
- *           computed in float32 on the GPU.  NULL skips them.
+ *           group): ||U||_F, ||W||_F^2, <W,O>_F, ||O||_F^2, ||O~||_F^2 (= ||O||^2
+ *           unless MuonGS), all computed in float32 on the GPU (W and O before
+ *           the update).  NULL skips them.
  *  Stream   a hipStream_t passed as void*; NULL is the default stream.  The
  *           call only enqueues work: it does not synchronise, allocate device
  *           memory or copy to the host.  Kernel faults surface at the
@@ -59,7 +60,7 @@
  *           muon_status_string() names a status.
  *  Hyperparameters  lr, momentum, weight_decay, a, b, c must be finite;
  *           ns_steps in [0, MUON_MAX_NS_STEPS]; ns_steps == 0 is legal and
- *           gives O = X0.  variant is MUON_VARIANT_MUON or _MUONGS.
+ *           gives O = X0.  variant: see MUON_VARIANT_* below.
  *  Shapes   1 <= rows, cols <= MUON_MAX_DIM.  An empty batch (count == 0 or
  *           ngroups == 0) is a no-op returning MUON_OK.
  *  Concurrency  calls on different streams must use different workspaces.
@@ -84,7 +85,20 @@ typedef enum muon_status {
 } muon_status;
 
 enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 };
-enum { MUON_VARIANT_MUON = 0, MUON_VARIANT_MUONGS = 1 };
+/*
+ * variant: one of
+ *   MUON_VARIANT_MUON    the step above;
+ *   MUON_VARIANT_MUONGS  with the Gram-Schmidt projection O~ (MuonGS page,
+ *                        "전제와 한계");
+ *   MUON_VARIANT_MUONH   fixed-radius control (the MuonH the MuonGS page
+ *                        compares against): W' = ||W||_F * W^ / ||W^||_F with
+ *                        W^ = (1 - lr*wd) W - lr*s*O, so ||W||_F never changes;
+ * optionally OR-ed with MUON_SCALE_KELLER to use Keller's shape factor
+ * s = max(1, rows/cols)^0.5 (last line of the loss-spike page's Newton-Schulz
+ * code block) instead of Moonlight's 0.2*sqrt(max(rows, cols)).
+ */
+enum { MUON_VARIANT_MUON = 0, MUON_VARIANT_MUONGS = 1, MUON_VARIANT_MUONH = 2 };
+#define MUON_SCALE_KELLER 0x100
 
 #define MUON_STATS_PER_MATRIX 5
 #define MUON_MAX_DIM 32768

@@ -21,6 +21,8 @@ MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
 MUON_VARIANT_MUON = 0
 MUON_VARIANT_MUONGS = 1
+MUON_VARIANT_MUONH = 2
+MUON_SCALE_KELLER = 0x100
 MUON_STATS_PER_MATRIX = 5
 MUON_MAX_DIM = 32768
 MUON_MAX_NS_STEPS = 100

@@ -21,7 +21,9 @@ import torch
 from . import _lib
 
 NS_COEFFICIENTS = (3.4445, -4.7750, 2.0315)
-VARIANTS = {"muon": _lib.MUON_VARIANT_MUON, "muongs": _lib.MUON_VARIANT_MUONGS}
+VARIANTS = {"muon": _lib.MUON_VARIANT_MUON, "muongs": _lib.MUON_VARIANT_MUONGS,
+            "muonh": _lib.MUON_VARIANT_MUONH}
+SCALES = {"moonlight": 0, "keller": _lib.MUON_SCALE_KELLER}
 _DTYPES = {torch.float32: _lib.MUON_DTYPE_F32, torch.bfloat16: _lib.MUON_DTYPE_BF16}
 
 
@@ -48,11 +50,14 @@ def dtype_code(dtype: torch.dtype) -> int:
         raise TypeError(f"Muon weights must be float32 or bfloat16, got {dtype}") from None
 
 
-def _variant_code(variant) -> int:
+def _variant_code(variant, scale="moonlight") -> int:
+    """variant name (or raw code) OR-ed with the shape-factor flag."""
+    if scale not in SCALES:
+        raise ValueError(f"unknown scale {scale!r}; expected one of {sorted(SCALES)}")
     if isinstance(variant, int):
-        return variant
+        return variant | SCALES[scale]
     try:
-        return VARIANTS[variant]
+        return VARIANTS[variant] | SCALES[scale]
     except KeyError:
         raise ValueError(f"unknown variant {variant!r}; expected one of {sorted(VARIANTS)}") from None
 
@@ -67,10 +72,11 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-def _scalars(dtype, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant):
+def _scalars(dtype, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant,
+             scale="moonlight"):
     a, b, c = ns_coefficients
     return [dtype, float(lr), float(momentum), float(weight_decay), int(ns_steps),
-            float(a), float(b), float(c), _variant_code(variant)]
+            float(a), float(b), float(c), _variant_code(variant, scale)]
 
 
 def _check_matrix(name, t, shape=None, dtype=None):
@@ -114,8 +120,8 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def muon_step(W, G, M, *, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
-              ns_coefficients=NS_COEFFICIENTS, variant="muon", workspace=None, stats=None,
-              stream=None):
+              ns_coefficients=NS_COEFFICIENTS, variant="muon", scale="moonlight", workspace=None,
+              stats=None, stream=None):
     """One Muon step on one matrix, in place on W and M.
 
     W, G: [rows, cols] float32 or bfloat16 on the GPU (same dtype); M float32.
@@ -133,7 +139,7 @@ def muon_step(W, G, M, *, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
         raise ValueError("stats must be a float32 GPU tensor with at least 5 elements")
     st = _lib.lib().muon_step(
         _ptr(W), _ptr(G), _ptr(M), rows, cols,
-        *_scalars(dt, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant),
+        *_scalars(dt, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant, scale),
         _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
     _check(st, "muon_step")
     return W, M
@@ -146,8 +152,8 @@ def pointer_table(tensors: Iterable[torch.Tensor], device) -> torch.Tensor:
 
 
 def muon_step_batched(Ws, Gs, Ms, *, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
-                      ns_coefficients=NS_COEFFICIENTS, variant="muon", workspace=None,
-                      stats=None, stream=None, tables=None):
+                      ns_coefficients=NS_COEFFICIENTS, variant="muon", scale="moonlight",
+                      workspace=None, stats=None, stream=None, tables=None):
     """One Muon step on a list of same-shape matrices (device pointer tables).
 
     ``tables`` may pass prebuilt (W, G, M) pointer tables to skip rebuilding.
@@ -171,7 +177,7 @@ def muon_step_batched(Ws, Gs, Ms, *, lr=0.02, momentum=0.95, weight_decay=0.1, n
     st = _lib.lib().muon_step_batched(
         _ptr(tables[0]), _ptr(tables[1]), _ptr(tables[2]), len(Ws), rows, cols,
         *_scalars(dtype_code(dtype), lr, momentum, weight_decay, ns_steps, ns_coefficients,
-                  variant),
+                  variant, scale),
         _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
     _check(st, "muon_step_batched")
 
@@ -196,8 +202,8 @@ def table_group(count, rows, cols, W_table, G_table, M_table) -> _lib.MuonGroup:
 
 def muon_step_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, lr=0.02,
                       momentum=0.95, weight_decay=0.1, ns_steps=5,
-                      ns_coefficients=NS_COEFFICIENTS, variant="muon", workspace=None,
-                      stats=None, stream=None, device=None):
+                      ns_coefficients=NS_COEFFICIENTS, variant="muon", scale="moonlight",
+                      workspace=None, stats=None, stream=None, device=None):
     """One Muon step over several shape groups (a whole model) in one launch
     sequence.  Build groups with :func:`stacked_group` / :func:`table_group`;
     the caller keeps the tensors they point to alive."""
@@ -210,7 +216,7 @@ def muon_step_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, l
     st = _lib.lib().muon_step_grouped(
         arr, len(groups),
         *_scalars(dtype_code(dtype), lr, momentum, weight_decay, ns_steps, ns_coefficients,
-                  variant),
+                  variant, scale),
         _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
     _check(st, "muon_step_grouped")
 
@@ -224,7 +230,7 @@ class MuonStep:
     """
 
     def __init__(self, params, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
-                 ns_coefficients=NS_COEFFICIENTS, variant="muon"):
+                 ns_coefficients=NS_COEFFICIENTS, variant="muon", scale="moonlight"):
         self.params = list(params)
         for i, p in enumerate(self.params):
             if p.ndim != 2:
@@ -232,7 +238,7 @@ class MuonStep:
                                  f"{p.ndim} dims (use AdamW for it)")
             _check_matrix(f"param[{i}]", p.data)
         self.hp = dict(lr=lr, momentum=momentum, weight_decay=weight_decay, ns_steps=ns_steps,
-                       ns_coefficients=tuple(ns_coefficients), variant=variant)
+                       ns_coefficients=tuple(ns_coefficients), variant=variant, scale=scale)
         self.momentum_buffers = [torch.zeros(p.shape, dtype=torch.float32, device=p.device)
                                  for p in self.params]
         self._by_dtype = {}

@@ -299,11 +299,19 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
   oo = block_sum_256(oo, red);
   if (threadIdx.x == 0) {
     const float coef = (variant == MUON_VARIANT_MUONGS && ww > 0.f) ? dot / ww : 0.f;
+    float hscale = 1.f;
+    if (variant == MUON_VARIANT_MUONH) {
+      // ||W^||^2 = ||d W - step O||^2 = d^2 ||W||^2 - 2 d step <W,O> + step^2 ||O||^2
+      const double d = g.decay, st = g.step;
+      const double h2 = d * d * double(ww) - 2.0 * d * st * double(dot) + st * st * double(oo);
+      if (h2 > 0.0) hscale = float(sqrt(double(ww) / h2));
+    }
     float* sc = g.scal + tr.m * kScal;
     sc[SC_R2] = ww;
     sc[SC_DOT] = dot;
     sc[SC_O2] = oo;
     sc[SC_COEF] = coef;
+    sc[SC_HSCALE] = hscale;
     if (g.stats) {
       float* st = g.stats + tr.m * MUON_STATS_PER_MATRIX;
       st[1] = ww;
@@ -314,10 +322,11 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
   }
 }
 
-// W' = (1 - lr*wd) W - lr*s*(O - coef*W), s = 0.2*sqrt(max(rows, cols)).
+// W' = h * ((1 - lr*wd) W - lr*s*(O - coef*W)): coef the MuonGS projection
+// coefficient, h the MuonH renormalisation (coef = 0, h = 1 for plain Muon).
 template <bool BF16>
 __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int ns_steps,
-                                                         int use_coef) {
+                                                         int reduced) {
   using E = Elem<BF16>;
   using TE = typename E::T;
   __shared__ float S[T][T + 1];
@@ -331,10 +340,11 @@ __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int 
   const TE* X = reinterpret_cast<const TE*>((ns_steps & 1) ? g.X1 : g.X0) + tr.m * g.x_stride;
   const float* sc = g.scal + tr.m * kScal;
   const float oscale = ns_steps == 0 ? sc[SC_INV] : 1.0f;
-  const float coef = use_coef ? sc[SC_COEF] : 0.f;
+  const float coef = reduced ? sc[SC_COEF] : 0.f;
+  const float h = reduced ? sc[SC_HSCALE] : 1.f;
   const float step = g.step;
-  const float wcoef = g.decay + step * coef;
-  const float ocoef = step * oscale;
+  const float wcoef = h * (g.decay + step * coef);
+  const float ocoef = h * step * oscale;
 
   float w[4][4], o[4][4];
   bool valid[4][4];
@@ -395,13 +405,13 @@ hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hi
 }
 
 hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,
-                             bool coef, hipStream_t s) {
+                             bool reduced, hipStream_t s) {
   if (bf16)
     hipLaunchKernelGGL(tail_apply_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, h.ns_steps,
-                       int(coef));
+                       int(reduced));
   else
     hipLaunchKernelGGL(tail_apply_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, h.ns_steps,
-                       int(coef));
+                       int(reduced));
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 //   tail_apply      W' = (1 - lr wd) W - lr s O~
 // Update order: "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저",
 // section 3 "Muon의 업데이트 순서".
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -92,7 +93,9 @@ int check_scalars(double lr, double momentum, double wd, int ns_steps, double a,
       !std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
     return MUON_ERR_INVALID_ARGUMENT;
   if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS) return MUON_ERR_INVALID_ARGUMENT;
-  if (variant != MUON_VARIANT_MUON && variant != MUON_VARIANT_MUONGS)
+  const int base = variant & 0xff;
+  if ((variant & ~(0xff | MUON_SCALE_KELLER)) != 0 ||
+      (base != MUON_VARIANT_MUON && base != MUON_VARIANT_MUONGS && base != MUON_VARIANT_MUONH))
     return MUON_ERR_INVALID_ARGUMENT;
   return MUON_OK;
 }
@@ -260,8 +263,9 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
   h.b = float(b);
   h.c = float(c);
   h.ns_steps = ns_steps;
-  h.variant = variant;
-  const bool reduce = variant == MUON_VARIANT_MUONGS || stats != nullptr;
+  h.variant = variant & 0xff;
+  const bool keller = (variant & MUON_SCALE_KELLER) != 0;
+  const bool reduce = h.variant != MUON_VARIANT_MUON || stats != nullptr;
 
   Sel sel[kMaxGroups];
   int nsel = 0;
@@ -323,7 +327,11 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       base += L.scal_bytes;
       m.stats = stats ? stats + sel[k].stats_index * MUON_STATS_PER_MATRIX : nullptr;
       m.decay = float(1.0 - lr * wd);
-      m.step = float(lr * 0.2 * std::sqrt(double(L.q)));
+      // Shape factor: Moonlight 0.2*sqrt(max(rows, cols)), or Keller
+      // max(1, rows/cols)^0.5.
+      const double sfac = keller ? std::sqrt(std::max(1.0, double(u.rows) / double(u.cols)))
+                                 : 0.2 * std::sqrt(double(L.q));
+      m.step = float(lr * sfac);
 
       const PhaseTiles pt = phase_tiles(L, dtype == MUON_DTYPE_BF16);
       w_head.tiles[k] = int(pt.head);
@@ -358,10 +366,9 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     }
     if (reduce) {
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, s), 5, s, t0))) return st;
-      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, variant, s), 6, s, t0))) return st;
+      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, s), 6, s, t0))) return st;
     }
-    if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h,
-                                                                     variant == MUON_VARIANT_MUONGS, s),
+    if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),
                                                    7, s, t0)))
       return st;
   }

@@ -53,7 +53,8 @@ enum : int {
   SC_R2 = 2,     // ||W||_F^2
   SC_DOT = 3,    // <W, O>_F
   SC_O2 = 4,     // ||O||_F^2
-  SC_COEF = 5,   // MuonGS projection coefficient <W,O>/||W||^2 (0 for Muon)
+  SC_COEF = 5,   // MuonGS projection coefficient <W,O>/||W||^2 (0 otherwise)
+  SC_HSCALE = 6, // MuonH renormalisation ||W|| / ||W^|| (1 otherwise)
   kScal = 8
 };
 
@@ -84,7 +85,7 @@ struct MatGroup {
   float* scal;
   float* stats;        // MUON_STATS_PER_MATRIX per matrix, or null
   float decay;         // 1 - lr*wd
-  float step;          // lr * 0.2 * sqrt(max(rows, cols))
+  float step;          // lr * s, s = 0.2*sqrt(max(rows, cols)) or max(1, rows/cols)^0.5
 };
 
 struct Batch {
@@ -174,8 +175,10 @@ hipError_t launch_norm_finalize(const Batch& bt, const Work& wk, hipStream_t s);
 hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps,
                               hipStream_t s);
 hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
+// `reduced`: tail_finalize ran, so the per-matrix coefficient and MuonH
+// scale are read from the scalars (otherwise 0 and 1).
 hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,
-                             bool coef, hipStream_t s);
+                             bool reduced, hipStream_t s);
 // Newton-Schulz products.  `iter` selects X0/X1 and the first-iteration norm
 // scaling.
 hipError_t launch_gram_bf16(const Batch& bt, const Work& wk, int iter, hipStream_t s);

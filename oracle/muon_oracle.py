@@ -61,6 +61,9 @@ RMS_MATCH = 0.2
 
 VARIANT_MUON = "muon"
 VARIANT_MUONGS = "muongs"
+VARIANT_MUONH = "muonh"
+SCALE_MOONLIGHT = "moonlight"
+SCALE_KELLER = "keller"
 
 
 def _f64(x) -> np.ndarray:
@@ -133,15 +136,34 @@ def muongs_project(W, O):
     return O - (frobenius_inner(W, O) / r2) * W
 
 
-def update_scale(rows, cols):
-    """Moonlight RMS matching, [MS] eq. 4: the factor 0.2 * sqrt(max(A, B))."""
-    return RMS_MATCH * float(np.sqrt(max(rows, cols)))
+def update_scale(rows, cols, scale=SCALE_MOONLIGHT):
+    """Shape factor of the update.
+
+    Moonlight RMS matching, [MS] eq. 4: 0.2 * sqrt(max(A, B)).
+    Keller's shape correction, the last line of the [LS] Newton-Schulz code
+    block: max(1, A/B)^0.5 with A x B the weight's own shape.
+    """
+    if scale == SCALE_MOONLIGHT:
+        return RMS_MATCH * float(np.sqrt(max(rows, cols)))
+    if scale == SCALE_KELLER:
+        return float(np.sqrt(max(1.0, rows / cols)))
+    raise ValueError(f"unknown scale {scale!r}")
+
+
+def muonh_renormalise(W, W_hat):
+    """MuonH, the fixed-radius control the [GS] page compares against
+    ("고정 반경 제약을 쓰는 MuonH"; fixed-norm control gives C_T = eta T / R):
+    the stepped weight is put back on the sphere of the weight's norm before
+    the step, R = ||W||_F:  W' = R * W_hat / ||W_hat||_F  (W_hat if zero)."""
+    R = np.sqrt(frobenius_inner(W, W))
+    n = np.sqrt(frobenius_inner(W_hat, W_hat))
+    return W_hat * (R / n) if n > 0 else W_hat
 
 
 def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
               weight_decay=DEFAULT_WEIGHT_DECAY, ns_steps=DEFAULT_NS_STEPS,
               a=NS_COEFFICIENTS[0], b=NS_COEFFICIENTS[1], c=NS_COEFFICIENTS[2],
-              variant=VARIANT_MUON, eps=NS_EPS):
+              variant=VARIANT_MUON, eps=NS_EPS, scale=SCALE_MOONLIGHT):
     """One Muon (or MuonGS) step on one 2-D hidden weight, in fp64.
 
     The order is [MX] section 3: momentum (Nesterov), magnitude normalisation,
@@ -152,8 +174,9 @@ def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
         M'  = mu M + G;  U = G + mu M'
         O   = NS_{a,b,c}^{ns_steps}(U)
         O~  = O - (<W,O>/||W||^2) W        (MuonGS only)
-        s   = 0.2 sqrt(max(A, B))
+        s   = 0.2 sqrt(max(A, B))           (or Keller's max(1, A/B)^0.5)
         W'  = (1 - lr*wd) W - lr * s * O~
+        W'  = ||W|| W' / ||W'||             (MuonH only)
 
     Returns (W', M', stats) where stats holds the scalars the library can
     report: norm_U = ||U||_F, r2 = ||W||_F^2, dot_WO = <W,O>_F,
@@ -167,15 +190,17 @@ def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
         raise ValueError("Muon updates 2-D weight matrices only")
     if G.shape != W.shape or M.shape != W.shape:
         raise ValueError("W, G and M must have the same shape")
-    if variant not in (VARIANT_MUON, VARIANT_MUONGS):
+    if variant not in (VARIANT_MUON, VARIANT_MUONGS, VARIANT_MUONH):
         raise ValueError(f"unknown variant {variant!r}")
     rows, cols = W.shape
 
     M_new, U = nesterov_momentum(G, M, momentum)
     O = newton_schulz(U, a, b, c, ns_steps, eps)
     O_t = muongs_project(W, O) if variant == VARIANT_MUONGS else O
-    s = update_scale(rows, cols)
+    s = update_scale(rows, cols, scale)
     W_new = (1.0 - lr * weight_decay) * W - lr * s * O_t
+    if variant == VARIANT_MUONH:
+        W_new = muonh_renormalise(W, W_new)
 
     stats = {
         "norm_U": float(np.linalg.norm(U, "fro")),

@@ -108,7 +108,8 @@ def call_step(L, W=W, G=G, M=M, rows=64, cols=128, dtype=0, ws=WS, wsb=1 << 30, 
     (dict(ns=-1), 1), (dict(ns=_lib.MUON_MAX_NS_STEPS + 1), 1),
     (dict(lr=float("nan")), 1), (dict(mom=float("inf")), 1), (dict(wd=float("-inf")), 1),
     (dict(a=float("nan")), 1), (dict(b=float("inf")), 1), (dict(c=float("nan")), 1),
-    (dict(variant=2), 1), (dict(variant=-1), 1),
+    (dict(variant=3), 1), (dict(variant=-1), 1), (dict(variant=0x200), 1),
+    (dict(variant=0x103), 1),
     (dict(ws=None), 1), (dict(wsb=1000), 4),
     (dict(G=W), 1),                          # W and G alias
     (dict(M=W + 64), 1),                     # M overlaps W
@@ -116,6 +117,12 @@ def call_step(L, W=W, G=G, M=M, rows=64, cols=128, dtype=0, ws=WS, wsb=1 << 30, 
 ])
 def test_step_validation(L, kw, status):
     assert call_step(L, **kw) == status
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 0x100, 0x101, 0x102])
+def test_valid_variants_pass_validation(L, variant):
+    """Valid variants get past argument checks (to the workspace check here)."""
+    assert call_step(L, variant=variant, wsb=16) == _lib.MUON_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_workspace_exact_size_boundary(L):

@@ -82,6 +82,32 @@ def test_bf16_ragged(shape, variant):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(96, 200), (200, 96), (128, 128)])
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_muonh(dtype, shape, wd):
+    """MuonH keeps ||W||_F: checked on the GPU output itself (bf16 rounding of
+    W' moves the norm by far less than 1e-3), and the update against the oracle."""
+    W, G, M = inputs(*shape, dtype, seed=77, m_std=1e-3)
+    W1, M1, st = gpu_step(W, G, M, variant="muonh", weight_decay=wd)
+    check_against_oracle(W, G, M, W1, M1, variant="muonh", stats=st, weight_decay=wd)
+    n0, n1 = np.linalg.norm(f64(W)), np.linalg.norm(f64(W1))
+    assert abs(n1 / n0 - 1) < (1e-6 if dtype == torch.float32 else 1e-3)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(256, 64), (64, 256), (130, 130)])
+@pytest.mark.parametrize("variant", ["muon", "muongs", "muonh"])
+def test_keller_scale(dtype, shape, variant):
+    """Keller's factor max(1, rows/cols)^0.5 is 1 for wide matrices (Moonlight's
+    would be 0.2*sqrt(256) = 3.2), so the bf16 update is 3x closer to a bf16
+    weight's resolution: the bf16 check adds the exact W' rounding cost."""
+    W, G, M = inputs(*shape, dtype, seed=78, m_std=1e-3)
+    W1, M1, st = gpu_step(W, G, M, variant=variant, scale="keller")
+    check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st, scale="keller",
+                         rounding_floor=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("ns", [0, 1, 2])
 def test_few_ns_steps(dtype, ns):
     """ns_steps = 0 returns the normalised look-ahead itself.  Its norm is 1

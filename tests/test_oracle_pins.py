@@ -339,3 +339,59 @@ def test_against_torch_optim_muon(shape):
         W, M, _ = muon_step(W, G, M, lr=0.02, momentum=0.95, weight_decay=0.1)
     got = p.detach().double().numpy()
     assert relerr(got - W0, W - W0) < 2e-2
+
+
+# ------------------------------------------- MuonH and Keller's shape scale
+@pytest.mark.parametrize("shape", [(16, 40), (40, 16), (24, 24)])
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_muonh_keeps_the_norm(shape, wd):
+    """MuonH holds ||W||_F fixed (the [GS] page's fixed-radius control), and
+    W' points along (1 - lr wd) W - lr s O."""
+    rng = np.random.default_rng(31)
+    W = rng.standard_normal(shape) * 0.02
+    G = rng.standard_normal(shape) * 1e-3
+    Wn, _, st = muon_step(W, G, np.zeros(shape), weight_decay=wd, variant="muonh")
+    assert abs(np.linalg.norm(Wn) / np.linalg.norm(W) - 1) < 1e-13
+    Wm, _, _ = muon_step(W, G, np.zeros(shape), weight_decay=wd, variant="muon")
+    cos = frobenius_inner(Wn, Wm) / (np.linalg.norm(Wn) * np.linalg.norm(Wm))
+    assert abs(cos - 1) < 1e-13
+
+
+def test_muonh_orthogonal_update_closed_form():
+    """O orthogonal to W (W chosen so), wd = 0: ||W - lr s O||^2 = r^2 +
+    (lr s)^2 ||O||^2, so W' = r (W - lr s O) / sqrt(r^2 + (lr s)^2 ||O||^2), and
+    the effective step size per unit radius is lr / r every step (C_T = lr T / R)."""
+    rng = np.random.default_rng(32)
+    shape = (12, 30)
+    Q = semi_orthogonal(*shape, rng)
+    W = rng.standard_normal(shape) * 0.02
+    W = W - frobenius_inner(W, Q) / frobenius_inner(Q, Q) * Q
+    r = np.linalg.norm(W)
+    Wn, _, _ = muon_step(W, Q, np.zeros(shape), weight_decay=0.0, variant="muonh")
+    O = newton_schulz(1.95 * Q, *NS_COEFFICIENTS, 5)
+    s = 0.2 * np.sqrt(30)
+    expect = r * (W - 0.02 * s * O) / np.sqrt(r ** 2 + (0.02 * s) ** 2 * np.sum(O ** 2))
+    assert relerr(Wn, expect) < 1e-12
+    # fixed radius: T steps accumulate C_T = sum lr/||W_t|| = lr T / r exactly
+    Wt, C = W, 0.0
+    for t in range(5):
+        C += 0.02 / np.linalg.norm(Wt)
+        Wt, _, _ = muon_step(Wt, rng.standard_normal(shape) * 1e-3, np.zeros(shape),
+                             weight_decay=0.0, variant="muonh")
+    assert abs(C / (0.02 * 5 / r) - 1) < 1e-12
+
+
+@pytest.mark.parametrize("shape,factor", [((64, 64), 1.0), ((256, 64), 2.0), ((64, 256), 1.0),
+                                          ((90, 10), 3.0)])
+def test_keller_shape_factor(shape, factor):
+    """[LS] code block, last line: update = X * max(1, rows/cols)^0.5."""
+    assert update_scale(*shape, scale="keller") == pytest.approx(factor, rel=0, abs=1e-15)
+    rng = np.random.default_rng(33)
+    W = rng.standard_normal(shape) * 0.02
+    G = rng.standard_normal(shape) * 1e-3
+    Wk, _, _ = muon_step(W, G, np.zeros(shape), scale="keller")
+    Wm, _, _ = muon_step(W, G, np.zeros(shape))
+    dk = Wk - (1 - 0.002) * W
+    dm = Wm - (1 - 0.002) * W
+    # same direction, magnitudes in the ratio of the two factors
+    assert relerr(dk, dm * factor / (0.2 * np.sqrt(max(shape)))) < 1e-12

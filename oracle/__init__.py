@@ -9,3 +9,6 @@ from .muon_oracle import (  # noqa: F401
     VARIANT_MUONGS, VARIANT_MUONH, frobenius_inner, muon_step, muongs_project,
     muonh_renormalise, nesterov_momentum, newton_schulz, update_scale,
 )
+from .adamw_oracle import (  # noqa: F401
+    AUX_BETAS, AUX_EPS, AUX_LR, AUX_WEIGHT_DECAY, adamw_step,
+)

@@ -16,6 +16,9 @@ resident in HBM.  Prints one JSON line:
               elementwise phases' GB/s vs HBM peak
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample of the
               same matrices, extrapolated to the full workload
+  aux_adamw   the other half of the hybrid optimizer, timed separately (not
+              part of `value`): one grouped AdamW call over the model's
+              embedding, head and gains, its GB/s against HBM peak
 """
 from __future__ import annotations
 
@@ -40,11 +43,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt160m")
-    ap.add_argument("--variant", default="muon", choices=["muon", "muongs"])
+    ap.add_argument("--variant", default="muon", choices=["muon", "muongs", "muonh"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-profile", action="store_true")
+    ap.add_argument("--no-aux", action="store_true", help="skip the AdamW-side measurement")
     return ap.parse_args()
 
 
@@ -109,6 +113,53 @@ def cpu_baseline(wl_mod, w, seconds):
             "sample": f"{done} of {w.n_matrices} matrices (round-robin over the shape groups), "
                       f"{spent:.1f} s of fp64 NumPy; seconds/step extrapolated per shape",
             "seconds_per_step": total, "host_cpus": os.cpu_count()}
+
+
+def aux_adamw(args, wl, dev, stream, muon_ms):
+    """AdamW over the workload's embedding, head and gains (bf16 parameters and
+    gradients, float32 moments): one grouped call per step, K timed calls
+    after W warm-up calls, each launch timed with HIP events."""
+    import torch
+    from muon_step_03_amd import AUX_LR, _lib, adamw_step_grouped, adamw_tensor
+    name = args.workload
+    Ps = wl.make_aux_params(name, dev)
+    Gs = wl.make_aux_grads(name, 1, dev)
+    mv = wl.make_aux_moments(name, dev)
+    roles = [t.role for t in wl.AUX_SETS[name]]
+    descs = [adamw_tensor(P, G, m, v, lr=AUX_LR[r]) for P, G, (m, v), r in zip(Ps, Gs, mv, roles)]
+    elems = sum(P.numel() for P in Ps)
+    state = {"t": 0}
+
+    def call():
+        state["t"] += 1
+        adamw_step_grouped(descs, torch.bfloat16, step=state["t"], stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    L = _lib.lib()
+    L.muon_profile_enable(1)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    L.muon_profile_enable(0)
+    n = _lib.MUON_NUM_PHASES
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    assert L.muon_profile_read(ms, cnt, n) == 0
+    k = [L.muon_phase_name(i).decode() for i in range(n)].index("adamw")
+    launch_ms = ms[k] / cnt[k]
+    call_ms = ms[k] / args.steps
+    nbytes = elems * (2 + 2 + 2 + 4 + 4 + 4 + 4)   # P r+w, G r, m r+w, v r+w
+    return {"tensors": len(Ps), "elements": elems, "launches_per_step": cnt[k] / args.steps,
+            "ms_per_step": call_ms, "wall_ms_per_step": wall_ms,
+            "avg_launch_ms": launch_ms, "alg_bytes_per_step": nbytes,
+            "gbps": nbytes / (call_ms * 1e-3) / 1e9,
+            "frac_of_hbm": nbytes / (call_ms * 1e-3) / PEAK_HBM,
+            "hybrid_ms_per_step": muon_ms + call_ms,
+            "hyper": {"betas": [0.8, 0.95], "eps": 1e-10, "weight_decay": 1e-3, "lr": AUX_LR}}
 
 
 def main():
@@ -207,6 +258,9 @@ def main():
         result["tail"] = {"ms": tail_ms, "gbps": work["tail_bytes"] / (tail_ms * 1e-3) / 1e9,
                           "frac_of_hbm": work["tail_bytes"] / (tail_ms * 1e-3) / PEAK_HBM}
         result["phase_ms_per_step"] = per_step
+
+    if not args.no_aux and args.workload in wl.AUX_SETS:
+        result["aux_adamw"] = aux_adamw(args, wl, dev, stream, ms_per_step)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_seconds)

@@ -1,7 +1,8 @@
 /*
- * muon.h — C ABI of the MI355X (gfx950) Muon optimizer step.
+ * muon.h — C ABI of the MI355X (gfx950) Muon optimizer step (and the AdamW
+ * step a hybrid Muon optimizer runs on its other parameters, declared below).
  *
- * One call performs one optimizer step on 2-D hidden-layer weight matrices:
+ * One Muon call performs one optimizer step on 2-D hidden-layer weight matrices:
  *
  *   M' = mu*M + G;  U = G + mu*M'                 momentum, Nesterov look-ahead
  *   X0 = U / (||U||_F + 1e-7)                     (U^T first if rows > cols)
@@ -156,17 +157,72 @@ int muon_step_grouped(const muon_group* groups, int ngroups, int dtype,
                       void* workspace, size_t workspace_bytes, float* stats, void* stream);
 
 /*
+ * AdamW for the parameters a hybrid Muon optimizer keeps off Muon: the input
+ * embedding, the output head and the gains and biases ("LLM Pretraining Loss
+ * Spike 진단과 처방" (juhoplayground.github.io), section "Muon head의 실체는
+ * 하이브리드 옵티마이저다"; "[Deep Learning] Muon" (codersblog.github.io),
+ * section 5 hands them to torch.optim.AdamW).  The MuonGS page's experiments
+ * paragraph ("전제와 한계") runs it with betas (0.8, 0.95), eps 1e-10, weight
+ * decay 1e-3 and peak learning rates 0.7 (embedding), 0.004 (head) and 0.015
+ * (1-D parameters).  The pages print no formula; this is textbook decoupled
+ * AdamW with bias correction, per element, in float32, at step t >= 1:
+ *
+ *   m' = beta1 m + (1 - beta1) g
+ *   v' = beta2 v + (1 - beta2) g^2
+ *   p' = (1 - lr wd) p - lr (m' / (1 - beta1^t)) / (sqrt(v' / (1 - beta2^t)) + eps)
+ *
+ *  Memory   P, G: DEVICE pointers to n contiguous elements of `dtype` (any
+ *           shape, flattened); m, v: DEVICE float32 arrays of n elements
+ *           (zero before the first step).  G is read only; P, m and v are
+ *           updated in place; P' is rounded to bfloat16 (nearest even) when
+ *           dtype is MUON_DTYPE_BF16.  No buffer may overlap another, within
+ *           a tensor or across the tensors of one call.  Any alignment works;
+ *           tensors whose four pointers are 8-byte (bf16) / 16-byte aligned
+ *           take the vector path.
+ *  Scalars  0 <= beta1, beta2 < 1; eps finite and >= 0; step >= 1 (it sets
+ *           the bias corrections); lr and weight_decay finite (any sign).
+ *  Sizes    0 <= n <= MUON_ADAMW_MAX_ELEMENTS; n == 0 skips the tensor.
+ *  Stream, errors  as for the Muon entry points: validated before anything
+ *           is enqueued, no allocation, no synchronisation.  The grouped call
+ *           updates all tensors in one launch per MUON_ADAMW_TENSORS_PER_LAUNCH
+ *           tensors (very large tensors are split over several slots).
+ */
+#define MUON_ADAMW_MAX_ELEMENTS (((int64_t)1) << 40)
+#define MUON_ADAMW_TENSORS_PER_LAUNCH 32
+
+typedef struct muon_adamw_tensor {
+  void* P;             /* parameters, `dtype` */
+  const void* G;       /* gradients, `dtype` */
+  float* m;            /* first moment, float32 */
+  float* v;            /* second moment, float32 */
+  int64_t n;           /* elements */
+  double lr;           /* learning rate of this tensor */
+  double weight_decay; /* decoupled weight decay of this tensor */
+} muon_adamw_tensor;
+
+/* One AdamW step on one tensor. */
+int muon_adamw_step(void* P, const void* G, float* m, float* v, int64_t n, int dtype,
+                    double lr, double beta1, double beta2, double eps, double weight_decay,
+                    int64_t step, void* stream);
+
+/* One AdamW step on `count` tensors with their own lr and weight decay and
+ * shared betas, eps and step.  `tensors` is a HOST array. */
+int muon_adamw_step_grouped(const muon_adamw_tensor* tensors, int64_t count, int dtype,
+                            double beta1, double beta2, double eps, int64_t step, void* stream);
+
+/*
  * Phase timing, for benchmarks and profiling.  While enabled (process-wide),
  * every kernel launch of the step entry points is bracketed by two HIP events
  * recorded on the caller's stream.  muon_profile_read waits for the recorded
  * events, adds each launch's elapsed milliseconds to ms_total[phase] and
  * launches[phase] (arrays of nphases entries, host memory, zeroed by the
  * caller), and forgets the records.  Phases: 0 head, 1 norm_finalize, 2 gram,
- * 3 poly, 4 update, 5 tail_reduce, 6 tail_finalize, 7 tail_apply.
+ * 3 poly, 4 update, 5 tail_reduce, 6 tail_finalize, 7 tail_apply, 8 adamw
+ * (the AdamW entry points).
  * Returns MUON_ERR_INVALID_ARGUMENT for null arrays or nphases < 1, and
  * MUON_ERR_HIP if an event call failed.
  */
-#define MUON_NUM_PHASES 8
+#define MUON_NUM_PHASES 9
 int muon_profile_enable(int enable);
 int muon_profile_read(double* ms_total, int64_t* launches, int nphases);
 /* Static name of a phase ("?" when out of range). */

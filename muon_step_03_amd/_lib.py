@@ -27,14 +27,17 @@ MUON_STATS_PER_MATRIX = 5
 MUON_MAX_DIM = 32768
 MUON_MAX_NS_STEPS = 100
 MUON_GROUPS_PER_LAUNCH = 8
+MUON_ADAMW_MAX_ELEMENTS = 1 << 40
+MUON_ADAMW_TENSORS_PER_LAUNCH = 32
 
 # Every symbol include/muon.h declares.
 EXPORTS = (
     "muon_workspace_bytes", "muon_workspace_bytes_grouped", "muon_step",
     "muon_step_batched", "muon_step_grouped", "muon_status_string", "muon_last_hip_error",
     "muon_profile_enable", "muon_profile_read", "muon_phase_name",
+    "muon_adamw_step", "muon_adamw_step_grouped",
 )
-MUON_NUM_PHASES = 8
+MUON_NUM_PHASES = 9
 
 
 class MuonGroup(ctypes.Structure):
@@ -48,6 +51,18 @@ class MuonGroup(ctypes.Structure):
         ("W", ctypes.c_void_p),
         ("G", ctypes.c_void_p),
         ("M", ctypes.c_void_p),
+    ]
+
+
+class AdamwTensor(ctypes.Structure):
+    _fields_ = [
+        ("P", ctypes.c_void_p),
+        ("G", ctypes.c_void_p),
+        ("m", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("lr", ctypes.c_double),
+        ("weight_decay", ctypes.c_double),
     ]
 
 
@@ -89,6 +104,15 @@ def lib():
     L.muon_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                     ctypes.c_int]
     L.muon_profile_read.restype = ctypes.c_int
+    L.muon_adamw_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                                  ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                  ctypes.c_double, ctypes.c_int64, ctypes.c_void_p]
+    L.muon_adamw_step.restype = ctypes.c_int
+    L.muon_adamw_step_grouped.argtypes = [ctypes.POINTER(AdamwTensor), ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                          ctypes.c_int64, ctypes.c_void_p]
+    L.muon_adamw_step_grouped.restype = ctypes.c_int
     L.muon_phase_name.argtypes = [ctypes.c_int]
     L.muon_phase_name.restype = ctypes.c_char_p
     _lib = L

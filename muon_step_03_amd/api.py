@@ -284,3 +284,114 @@ class MuonStep:
                 self._workspaces[dtype] = ws
             muon_step_grouped(groups, dtype, workspace=ws, stats=stats, device=ws.device,
                               **self.hp)
+
+
+# ---------------------------------------------------------------- AdamW half
+# The hybrid optimizer's AdamW for embeddings, output head and 1-D parameters
+# ("LLM Pretraining Loss Spike 진단과 처방", section "Muon head의 실체는 하이브리드
+# 옵티마이저다").  Defaults from the experiments paragraph of "MuonGS:
+# Pretraining LLMs with Relaxed Weight-Norm Control": betas (0.8, 0.95),
+# eps 1e-10, weight decay 1e-3, peak lrs 0.7 / 0.004 / 0.015 for embedding /
+# head / 1-D parameters.
+AUX_BETAS = (0.8, 0.95)
+AUX_EPS = 1e-10
+AUX_WEIGHT_DECAY = 1e-3
+AUX_LR = {"embedding": 0.7, "head": 0.004, "vector": 0.015}
+
+
+def _check_flat(name, t, numel=None, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def adamw_tensor(P, G, m, v, *, lr, weight_decay=AUX_WEIGHT_DECAY) -> _lib.AdamwTensor:
+    """Descriptor of one tensor for :func:`adamw_step_grouped` (the caller
+    keeps P, G, m, v alive until the step has run)."""
+    _check_flat("P", P)
+    dtype_code(P.dtype)
+    _check_flat("G", G, P.numel(), P.dtype)
+    _check_flat("m", m, P.numel(), torch.float32)
+    _check_flat("v", v, P.numel(), torch.float32)
+    return _lib.AdamwTensor(P.data_ptr(), G.data_ptr(), m.data_ptr(), v.data_ptr(), P.numel(),
+                            float(lr), float(weight_decay))
+
+
+def adamw_step(P, G, m, v, *, lr, step, betas=AUX_BETAS, eps=AUX_EPS,
+               weight_decay=AUX_WEIGHT_DECAY, stream=None):
+    """One AdamW step on one tensor, in place on P, m and v.  ``step`` counts
+    updates from 1 (bias corrections)."""
+    t = adamw_tensor(P, G, m, v, lr=lr, weight_decay=weight_decay)
+    st = _lib.lib().muon_adamw_step(t.P, t.G, t.m, t.v, t.n, dtype_code(P.dtype), t.lr,
+                                    float(betas[0]), float(betas[1]), float(eps),
+                                    t.weight_decay, int(step), _stream_handle(stream))
+    _check(st, "muon_adamw_step")
+
+
+def adamw_step_grouped(tensors: Sequence[_lib.AdamwTensor], dtype: torch.dtype, *, step,
+                       betas=AUX_BETAS, eps=AUX_EPS, stream=None):
+    """One AdamW step on many tensors of one dtype, one launch per
+    ``MUON_ADAMW_TENSORS_PER_LAUNCH`` tensors."""
+    tensors = list(tensors)
+    arr = (_lib.AdamwTensor * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i] = t
+    st = _lib.lib().muon_adamw_step_grouped(arr, len(tensors), dtype_code(dtype),
+                                            float(betas[0]), float(betas[1]), float(eps),
+                                            int(step), _stream_handle(stream))
+    _check(st, "muon_adamw_step_grouped")
+
+
+class AdamWStep:
+    """AdamW over parameter groups (dicts with ``params``, ``lr`` and optional
+    ``weight_decay``), float32 moments per parameter, every parameter of one
+    dtype updated by one grouped call per step from its ``.grad``."""
+
+    def __init__(self, param_groups, betas=AUX_BETAS, eps=AUX_EPS,
+                 weight_decay=AUX_WEIGHT_DECAY):
+        self.betas = tuple(betas)
+        self.eps = float(eps)
+        self.entries = []   # (param, m, v, lr, weight_decay)
+        for gi, grp in enumerate(param_groups):
+            lr = grp["lr"]
+            wd = grp.get("weight_decay", weight_decay)
+            for p in grp["params"]:
+                _check_flat(f"group {gi} param", p.data)
+                dtype_code(p.dtype)
+                self.entries.append((p, torch.zeros(p.numel(), dtype=torch.float32, device=p.device),
+                                     torch.zeros(p.numel(), dtype=torch.float32, device=p.device),
+                                     lr, wd))
+        self.step_count = 0
+
+    @torch.no_grad()
+    def step(self):
+        self.step_count += 1
+        by_dtype = {}
+        for i, (p, m, v, lr, wd) in enumerate(self.entries):
+            if p.grad is None:
+                raise RuntimeError(f"AdamW parameter {i} has no gradient")
+            by_dtype.setdefault(p.dtype, []).append(
+                adamw_tensor(p.data, p.grad, m, v, lr=lr, weight_decay=wd))
+        for dtype, tensors in by_dtype.items():
+            adamw_step_grouped(tensors, dtype, step=self.step_count, betas=self.betas, eps=self.eps)
+
+
+class HybridMuonAdamW:
+    """The hybrid the pages describe: Muon on hidden 2-D weights, AdamW on
+    everything else (embedding, head, gains, biases).  ``muon_params`` go to
+    :class:`MuonStep`, ``adamw_groups`` to :class:`AdamWStep`."""
+
+    def __init__(self, muon_params, adamw_groups, *, muon_kwargs=None, adamw_kwargs=None):
+        self.muon = MuonStep(muon_params, **(muon_kwargs or {}))
+        self.adamw = AdamWStep(adamw_groups, **(adamw_kwargs or {}))
+
+    def step(self, stats=None):
+        self.muon.step(stats=stats)
+        self.adamw.step()

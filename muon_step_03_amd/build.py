@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmuon.so")
 
-SOURCES = ["muon_abi.hip", "k_elementwise.hip", "k_ns_bf16.hip", "k_ns_f32.hip"]
+SOURCES = ["muon_abi.hip", "k_elementwise.hip", "k_ns_bf16.hip", "k_ns_f32.hip", "k_adamw.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -56,7 +56,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

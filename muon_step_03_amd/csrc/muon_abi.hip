@@ -141,8 +141,11 @@ PhaseTiles phase_tiles(const Layout& L, bool bf16) {
   return t;
 }
 
-const char* kPhaseNames[] = {"head", "norm_finalize", "gram", "poly", "update",
-                             "tail_reduce", "tail_finalize", "tail_apply"};
+const char* kPhaseNames[] = {"head",        "norm_finalize", "gram",       "poly",  "update",
+                             "tail_reduce", "tail_finalize", "tail_apply", "adamw"};
+static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == MUON_NUM_PHASES,
+              "one name per phase");
+constexpr int kPhaseAdamw = 8;
 
 // ---- optional phase timing (HIP events around each launch)
 struct ProfRecord {
@@ -375,9 +378,132 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
   return MUON_OK;
 }
 
+// ---- AdamW over many tensors
+// A tensor is split into segments of at most kAdamSegMaxBlocks blocks, and a
+// launch takes up to kAdamSegs segments and at most kMaxBlocks blocks.
+constexpr int64_t kAdamSegMaxBlocks = int64_t(1) << 22;
+
+int check_adamw_scalars(double beta1, double beta2, double eps, int64_t step) {
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0)) return MUON_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(eps) || eps < 0.0) return MUON_ERR_INVALID_ARGUMENT;
+  if (step < 1) return MUON_ERR_INVALID_ARGUMENT;
+  return MUON_OK;
+}
+
+int check_adamw_tensors(const muon_adamw_tensor* t, int64_t count, int dtype) {
+  if (count < 0 || (count > 0 && !t)) return MUON_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype == MUON_DTYPE_BF16 ? 2 : 4;
+  struct Range {
+    uintptr_t lo, hi;
+  };
+  std::vector<Range> r;
+  r.reserve(size_t(count) * 4);
+  for (int64_t i = 0; i < count; ++i) {
+    const muon_adamw_tensor& x = t[i];
+    if (!std::isfinite(x.lr) || !std::isfinite(x.weight_decay)) return MUON_ERR_INVALID_ARGUMENT;
+    if (x.n < 0 || x.n > MUON_ADAMW_MAX_ELEMENTS) return MUON_ERR_INVALID_SHAPE;
+    if (x.n == 0) continue;
+    if (!x.P || !x.G || !x.m || !x.v) return MUON_ERR_INVALID_ARGUMENT;
+    const size_t n = size_t(x.n);
+    r.push_back({reinterpret_cast<uintptr_t>(x.P), reinterpret_cast<uintptr_t>(x.P) + n * es});
+    r.push_back({reinterpret_cast<uintptr_t>(x.G), reinterpret_cast<uintptr_t>(x.G) + n * es});
+    r.push_back({reinterpret_cast<uintptr_t>(x.m), reinterpret_cast<uintptr_t>(x.m) + n * 4});
+    r.push_back({reinterpret_cast<uintptr_t>(x.v), reinterpret_cast<uintptr_t>(x.v) + n * 4});
+  }
+  // No buffer of any tensor may overlap another buffer (of the same or of
+  // another tensor): sorted by start, each range must end before the next.
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i)
+    if (r[i].lo < r[i - 1].hi) return MUON_ERR_INVALID_ARGUMENT;
+  return MUON_OK;
+}
+
+int run_adamw(const muon_adamw_tensor* t, int64_t count, int dtype, double beta1, double beta2,
+              double eps, int64_t step, void* stream) {
+  if (!dtype_ok(dtype)) return MUON_ERR_UNSUPPORTED_DTYPE;
+  int st = check_adamw_scalars(beta1, beta2, eps, step);
+  if (st != MUON_OK) return st;
+  st = check_adamw_tensors(t, count, dtype);
+  if (st != MUON_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const bool bf16 = dtype == MUON_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  // Bias corrections in double: 1 - beta^t.
+  const double bc1 = 1.0 - std::pow(beta1, double(step));
+  const double bc2 = 1.0 - std::pow(beta2, double(step));
+  AdamBatch bt;
+  std::memset(&bt, 0, sizeof(bt));
+  bt.beta1 = float(beta1);
+  bt.beta2 = float(beta2);
+  bt.one_minus_beta1 = float(1.0 - beta1);
+  bt.one_minus_beta2 = float(1.0 - beta2);
+  bt.eps = float(eps);
+  bt.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+
+  auto flush = [&]() -> int {
+    if (bt.nseg == 0) return MUON_OK;
+    hipEvent_t t0 = prof_start(s);
+    const int r = finish_launch(launch_adamw(bt, bf16, s), kPhaseAdamw, s, t0);
+    bt.nseg = 0;
+    bt.begin[0] = 0;
+    return r;
+  };
+  for (int64_t i = 0; i < count; ++i) {
+    const muon_adamw_tensor& x = t[i];
+    if (x.n == 0) continue;
+    const uintptr_t vp = reinterpret_cast<uintptr_t>(x.P), vg = reinterpret_cast<uintptr_t>(x.G);
+    const uintptr_t vm = reinterpret_cast<uintptr_t>(x.m), vv = reinterpret_cast<uintptr_t>(x.v);
+    const size_t va = es * kAdamVec;
+    const int vec = (vp % va == 0 && vg % va == 0 && vm % 16 == 0 && vv % 16 == 0) ? 1 : 0;
+    const float decay = float(1.0 - x.lr * x.weight_decay);
+    const float step_size = float(x.lr / bc1);
+    for (int64_t off = 0; off < x.n;) {
+      const int64_t blocks = std::min(cdiv(x.n - off, kAdamChunk), kAdamSegMaxBlocks);
+      if (bt.nseg == kAdamSegs || bt.begin[bt.nseg] + blocks > kMaxBlocks) {
+        if ((st = flush()) != MUON_OK) return st;
+      }
+      const int64_t n = std::min(x.n - off, blocks * int64_t(kAdamChunk));
+      AdamSeg& g = bt.seg[bt.nseg];
+      g.P = static_cast<char*>(x.P) + size_t(off) * es;
+      g.G = static_cast<const char*>(x.G) + size_t(off) * es;
+      g.m = x.m + off;
+      g.v = x.v + off;
+      g.n = n;
+      g.decay = decay;
+      g.step_size = step_size;
+      g.vec = vec;
+      bt.begin[bt.nseg + 1] = bt.begin[bt.nseg] + blocks;
+      ++bt.nseg;
+      off += n;
+    }
+  }
+  return flush();
+}
+
 }  // namespace
 
 extern "C" {
+
+int muon_adamw_step(void* P, const void* G, float* m, float* v, int64_t n, int dtype, double lr,
+                    double beta1, double beta2, double eps, double weight_decay, int64_t step,
+                    void* stream) {
+  muon_adamw_tensor t{};
+  t.P = P;
+  t.G = G;
+  t.m = m;
+  t.v = v;
+  t.n = n;
+  t.lr = lr;
+  t.weight_decay = weight_decay;
+  return run_adamw(&t, 1, dtype, beta1, beta2, eps, step, stream);
+}
+
+int muon_adamw_step_grouped(const muon_adamw_tensor* tensors, int64_t count, int dtype,
+                            double beta1, double beta2, double eps, int64_t step, void* stream) {
+  return run_adamw(tensors, count, dtype, beta1, beta2, eps, step, stream);
+}
 
 size_t muon_workspace_bytes(int64_t count, int64_t rows, int64_t cols, int dtype) {
   if (!dtype_ok(dtype) || count < 0) return 0;

@@ -168,6 +168,35 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// ---------------------------------------------------------------- AdamW
+// One launch covers up to kAdamSegs parameter tensors; each block updates
+// kAdamChunk consecutive elements of one tensor.
+constexpr int kAdamSegs = MUON_ADAMW_TENSORS_PER_LAUNCH;
+constexpr int kAdamVec = 4;                    // elements per vector access
+constexpr int kAdamVecPerThread = 4;           // vectors per thread per block
+constexpr int kAdamChunk = 256 * kAdamVec * kAdamVecPerThread;
+
+struct AdamSeg {
+  void* P;              // parameters (bf16 bits or float)
+  const void* G;        // gradients, same dtype as P
+  float* m;             // first moment
+  float* v;             // second moment
+  int64_t n;            // elements
+  float decay;          // 1 - lr*wd
+  float step_size;      // lr / (1 - beta1^t)
+  int vec;              // 1: all four pointers allow kAdamVec-wide accesses
+  int pad_;
+};
+
+struct AdamBatch {
+  AdamSeg seg[kAdamSegs];
+  int64_t begin[kAdamSegs + 1];  // blocks of tensor s are [begin[s], begin[s+1])
+  int nseg;
+  float beta1, beta2, eps;
+  float one_minus_beta1, one_minus_beta2;  // rounded once from double (not 1 - float(beta))
+  float inv_sqrt_bc2;            // 1 / sqrt(1 - beta2^t)
+};
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_head(const Batch& bt, const Work& wk, bool bf16, float momentum, hipStream_t s);
@@ -187,5 +216,7 @@ hipError_t launch_update_bf16(const Batch& bt, const Work& wk, int iter, float a
 hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s);
 hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
 hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);
+// AdamW over the tensors of `bt`: begin[nseg] blocks.
+hipError_t launch_adamw(const AdamBatch& bt, bool bf16, hipStream_t s);
 
 }  // namespace muon

@@ -21,6 +21,7 @@ group is reproducible on its own.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
 
 import torch
@@ -156,3 +157,69 @@ def random_matrix(rows, cols, std, seed, dtype=torch.float32, device="cpu"):
     x = torch.empty((rows, cols), dtype=torch.float32, device=device)
     x.normal_(0.0, std, generator=gen)
     return x.to(dtype)
+
+
+# ------------------------------------------------------- AdamW-side tensors
+# The parameters the hybrid optimizer gives to AdamW: input embedding, output
+# head (untied) and the 1-D gains, two per layer plus a final one.  The pages
+# give no vocabulary size; 50304 (GPT-2's 50257 tokens padded to a multiple
+# of 128, as NanoGPT-family models do) stands in.  Roles select the
+# per-tensor learning rate (embedding / head / vector).
+AUX_VOCAB = 50304
+
+
+@dataclass(frozen=True)
+class AuxTensor:
+    role: str      # "embedding", "head" or "vector"
+    shape: tuple
+
+
+def _aux(hidden, n_layers):
+    return ((AuxTensor("embedding", (AUX_VOCAB, hidden)), AuxTensor("head", (AUX_VOCAB, hidden)))
+            + tuple(AuxTensor("vector", (hidden,)) for _ in range(2 * n_layers + 1)))
+
+
+AUX_SETS = {
+    "gpt160m": _aux(768, 12),
+    "gpt400m": _aux(1024, 24),
+    "moe1b": _aux(512, 32),
+}
+
+
+def aux_seed(workload_index: int, step: int, kind: int) -> int:
+    """Seed of the generator that draws every AdamW-side tensor of one kind
+    (0 parameters, 1 gradients), in table order."""
+    return 1_000_000 + 1000 * workload_index + 10 * step + kind
+
+
+def make_aux_params(name: str, device="cpu", dtype=BF16):
+    """Embedding and head ~ N(0, 0.02^2); gains ~ 1 + N(0, 0.02^2)."""
+    wl = WORKLOADS[name]
+    gen = _gen(device, aux_seed(wl.index, 0, 0))
+    out = []
+    for t in AUX_SETS[name]:
+        x = torch.empty(t.shape, dtype=torch.float32, device=device)
+        x.normal_(0.0, W_STD, generator=gen)
+        if t.role == "vector":
+            x.add_(1.0)
+        out.append(x.to(torch_dtype(dtype)))
+    return out
+
+
+def make_aux_grads(name: str, step: int = 0, device="cpu", dtype=BF16):
+    """Gradients ~ N(0, (1e-3)^2)."""
+    wl = WORKLOADS[name]
+    gen = _gen(device, aux_seed(wl.index, step, 1))
+    out = []
+    for t in AUX_SETS[name]:
+        x = torch.empty(t.shape, dtype=torch.float32, device=device)
+        x.normal_(0.0, G_STD, generator=gen)
+        out.append(x.to(torch_dtype(dtype)))
+    return out
+
+
+def make_aux_moments(name: str, device="cpu"):
+    """First and second moments start at zero (float32, flattened)."""
+    return [(torch.zeros(math.prod(t.shape), dtype=torch.float32, device=device),
+             torch.zeros(math.prod(t.shape), dtype=torch.float32, device=device))
+            for t in AUX_SETS[name]]

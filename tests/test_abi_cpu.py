@@ -172,8 +172,8 @@ def test_grouped_validation(L):
 def test_phase_names_and_profile_args(L):
     names = [L.muon_phase_name(i).decode() for i in range(_lib.MUON_NUM_PHASES)]
     assert names == ["head", "norm_finalize", "gram", "poly", "update", "tail_reduce",
-                     "tail_finalize", "tail_apply"]
-    assert L.muon_phase_name(8) == b"?" and L.muon_phase_name(-1) == b"?"
+                     "tail_finalize", "tail_apply", "adamw"]
+    assert L.muon_phase_name(9) == b"?" and L.muon_phase_name(-1) == b"?"
     assert L.muon_profile_read(None, None, 8) == 1
     ms = (ctypes.c_double * 8)()
     n = (ctypes.c_int64 * 8)()
@@ -189,3 +189,72 @@ def test_python_binding_rejects_non_2d():
         MuonStep([torch.nn.Parameter(torch.zeros(8))])
     with pytest.raises(ValueError):
         muon_step(torch.zeros(4, 4, 4), torch.zeros(4, 4, 4), torch.zeros(4, 4, 4))
+
+
+# ------------------------------------------------------------ AdamW entry points
+P_, G_, MM, VV = 0x50000000, 0x60000000, 0x70000000, 0x80000000
+ADAM_OK = dict(lr=0.015, b1=0.8, b2=0.95, eps=1e-10, wd=1e-3, step=1)
+
+
+def call_adamw(L, P=P_, G=G_, m=MM, v=VV, n=1000, dtype=1, **kw):
+    k = dict(ADAM_OK, **kw)
+    return L.muon_adamw_step(P, G, m, v, n, dtype, k["lr"], k["b1"], k["b2"], k["eps"], k["wd"],
+                             k["step"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(b1=1.0), 1), (dict(b1=-0.1), 1), (dict(b2=1.0), 1), (dict(b2=float("nan")), 1),
+    (dict(eps=-1e-10), 1), (dict(eps=float("inf")), 1), (dict(step=0), 1), (dict(step=-3), 1),
+    (dict(lr=float("nan")), 1), (dict(wd=float("inf")), 1),
+    (dict(n=-1), 2), (dict(n=(1 << 40) + 1), 2),
+    (dict(P=None), 1), (dict(G=None), 1), (dict(m=None), 1), (dict(v=None), 1),
+    # overlapping buffers: G inside P (bf16: 2000 bytes), v inside m (4000 bytes)
+    (dict(G=P_ + 1998), 1), (dict(v=MM + 3996), 1), (dict(m=G_), 1),
+])
+def test_adamw_validation(L, kw, status):
+    assert call_adamw(L, **kw) == status
+
+
+def test_adamw_empty_is_noop(L):
+    """n == 0 (any pointers) and an empty group enqueue nothing."""
+    assert call_adamw(L, n=0, P=None, G=None, m=None, v=None) == 0
+    assert L.muon_adamw_step_grouped(None, 0, 1, 0.8, 0.95, 1e-10, 1, None) == 0
+
+
+def test_adamw_grouped_validation(L):
+    T = _lib.AdamwTensor
+    arr = lambda *t: (T * len(t))(*t)  # noqa: E731
+    a = T(P_, G_, MM, VV, 1000, 0.7, 1e-3)
+    b = T(P_ + 4096, G_ + 4096, MM + 8192, VV + 8192, 1000, 0.004, 1e-3)
+    args = (1, 0.8, 0.95, 1e-10, 1, None)
+    assert L.muon_adamw_step_grouped(None, 2, *args) == 1
+    assert L.muon_adamw_step_grouped(arr(a, b), -1, *args) == 1
+    # one tensor's v overlaps the other's m
+    c = T(P_ + 4096, G_ + 4096, MM + 8192, MM + 100, 1000, 0.004, 1e-3)
+    assert L.muon_adamw_step_grouped(arr(a, c), 2, *args) == 1
+    # the same tensor twice aliases every buffer
+    assert L.muon_adamw_step_grouped(arr(a, a), 2, *args) == 1
+    bad = T(P_ + 4096, G_ + 4096, MM + 8192, VV + 8192, 1000, float("nan"), 1e-3)
+    assert L.muon_adamw_step_grouped(arr(a, bad), 2, *args) == 1
+    # disjoint tensors with n == 0 entries: only the scalars fail here
+    z = T(None, None, None, None, 0, 0.1, 0.0)
+    assert L.muon_adamw_step_grouped(arr(z, a, b), 3, 1, 1.5, 0.95, 1e-10, 1, None) == 1
+    assert L.muon_adamw_step_grouped(arr(z, a, b), 3, 7, 0.8, 0.95, 1e-10, 1, None) == 3
+
+
+def test_adamw_python_binding_checks():
+    torch = pytest.importorskip("torch")
+    from muon_step_03_amd import AdamWStep, adamw_tensor
+    with pytest.raises(ValueError):   # CPU tensors are rejected before any library call
+        adamw_tensor(torch.zeros(4), torch.zeros(4), torch.zeros(4), torch.zeros(4), lr=0.1)
+    with pytest.raises(ValueError):
+        AdamWStep([dict(params=[torch.nn.Parameter(torch.zeros(4))], lr=0.1)])
+
+
+def test_aux_workload_matches_page_hyperparameters():
+    """The binding's AdamW defaults are the oracle's (pinned to the pages)."""
+    import oracle
+    from muon_step_03_amd import api
+    assert api.AUX_BETAS == oracle.AUX_BETAS and api.AUX_EPS == oracle.AUX_EPS
+    assert api.AUX_WEIGHT_DECAY == oracle.AUX_WEIGHT_DECAY and api.AUX_LR == oracle.AUX_LR

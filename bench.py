@@ -49,7 +49,58 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-profile", action="store_true")
     ap.add_argument("--no-aux", action="store_true", help="skip the AdamW-side measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_update_gpt160m_hbm_traffic.md")
+# The sources the update kernel is built from: traffic counters are only
+# reported while these are unchanged since the counters were taken.
+KERNEL_SOURCES = ("muon_step_03_amd/csrc/k_ns_bf16.hip", "muon_step_03_amd/csrc/muon_internal.h")
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per update launch from the committed counter summary, or
+    None if there is none for this workload or the kernel has changed."""
+    if workload != "gpt160m" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "traffic_bytes_per_launch", "kernel_source_sha256"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
 def matrix_work(groups, dtype_bytes):
@@ -170,6 +221,9 @@ def main():
               f"{world}): this build has no multi-GPU path; each GPU would run the same "
               "step on its own share of the matrices.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     from muon_step_03_amd import _lib, muon_step_grouped, stacked_group, workspace_bytes_grouped
@@ -243,7 +297,7 @@ def main():
         result["roofline"] = {
             "kernel": "ns_update (X' = aX + B X)", "bound": "mfma",
             "achieved": a / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s", "frac": a / peak,
-            "traffic": None, "avg_launch_ms": avg["update"],
+            "traffic": measured_traffic(w.name), "avg_launch_ms": avg["update"],
             "alg_flops_per_launch": upd_flops,
         }
         ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"]

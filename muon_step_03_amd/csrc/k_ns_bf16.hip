@@ -17,14 +17,21 @@
 // ||U|| while it writes X0): its Gram is scaled by inv^2 and its update by
 // inv, inv = 1/(||U||_F + 1e-7), which is the iteration applied to U*inv.
 //
-// Kernel structure (256 threads = 4 waves in a 2x2 grid):
+// Kernel structure (defaults: 256 threads = 4 waves in a 2x2 grid):
 //  * Block tiles are compile-time (defaults: symmetric products 128x128,
-//    64x64 per wave; update 128x256, 64x128 per wave, fewer LDS reads per
-//    MFMA).
+//    64x64 per wave; update 128x256, 64x128 per wave).
 //  * K steps of 32, staged through LDS by 16-byte direct-to-LDS loads
 //    (global_load_lds): STAGES buffers, loads for up to STAGES-1 later steps
 //    in flight while step k is multiplied; one barrier per K step, and the
-//    MFMA fragments double-buffered in registers.
+//    MFMA fragments double-buffered in registers.  The loads address memory
+//    as a scalar base (advanced once per K step) plus a per-lane offset
+//    fixed for the tile, and the K loop is unrolled by STAGES so that every
+//    LDS address is a lane's base plus an immediate: the loop body issues
+//    MFMAs, LDS reads and loads with almost no vector address arithmetic.
+//  * Epilogue: the fp32 tile is staged through LDS in 64-row passes and
+//    stored as 16-byte rows of 8 bf16; the linear terms (a*X of the update,
+//    b*A of the polynomial) are read there as 16-byte rows of the operand
+//    (L2-resident), so the K loop carries nothing but the product.
 //  * K-contiguous operand tiles: rows of 32 bf16 (64 B, 4 chunks of 16 B),
 //    chunk c of row m stored at c ^ f(m), f(m) = ((m>>1) + (m>>3)) & 3,
 //    so the fragment reads (32 consecutive rows, one chunk) do not collide
@@ -37,9 +44,13 @@
 //    ds_read_b64_tr_b16: within a 16-lane group, output lane i element j
 //    comes from source lane 4j + i/4, element i%4, so lane s addresses
 //    X[k0 + s/4][n0 + 4 (s%4)] and two reads give 8 consecutive k.
-//  * Blocks are renumbered so that consecutive tiles (same matrix) land on
-//    the same XCD (hardware dispatches block b to XCD b % 8), keeping one
-//    matrix's operands in one XCD's L2.
+//  * Persistent blocks (two per CU) walk a static tile list: XCD x (the
+//    hardware dispatches block b to XCD b % 8) takes one contiguous eighth of
+//    every group's tiles, so its blocks work on consecutive tiles of one
+//    matrix at a time and share its operands in that XCD's L2; a block's
+//    next tile loads while its previous tile's stores drain.
+#include <type_traits>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -65,25 +76,28 @@ struct Cfg;
 #ifndef MUON_UPD_STAGES
 #define MUON_UPD_STAGES 3
 #endif
-#ifndef MUON_SYRK_OCC
-#define MUON_SYRK_OCC 2
+// Wave grid of the update block: WGM rows of waves.
+#ifndef MUON_UPD_WGM
+#define MUON_UPD_WGM 2
 #endif
-#ifndef MUON_UPD_OCC
-#define MUON_UPD_OCC 2
-#endif
+// NW waves in a WGM x WGN grid; each wave holds WM x WN accumulators of
+// 32x32; OCC blocks per CU (the register and LDS budget).
 template <>
 struct Cfg<MODE_GRAM> {
-  static constexpr int BM = kSyrkTile, BN = kSyrkTile, WM = BM / 64, WN = BN / 64;
+  static constexpr int BM = kSyrkTile, BN = kSyrkTile, NW = 4, WGM = 2, WGN = 2;
+  static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
   static constexpr int STAGES = MUON_SYRK_STAGES;
-  static constexpr int OCC = MUON_SYRK_OCC;  // blocks per CU the register budget targets
+  static constexpr int OCC = kSyrkBlocksPerCU;
 };
 template <>
 struct Cfg<MODE_POLY> : Cfg<MODE_GRAM> {};
 template <>
 struct Cfg<MODE_UPDATE> {
-  static constexpr int BM = kUpdTileM, BN = kUpdTileN, WM = BM / 64, WN = BN / 64;
+  static constexpr int BM = kUpdTileM, BN = kUpdTileN, NW = kUpdWaves, WGM = MUON_UPD_WGM,
+                       WGN = NW / WGM;
+  static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
   static constexpr int STAGES = MUON_UPD_STAGES;
-  static constexpr int OCC = MUON_UPD_OCC;
+  static constexpr int OCC = kUpdBlocksPerCU;
 };
 
 __device__ __forceinline__ int fswz(int m) { return ((m >> 1) + (m >> 3)) & 3; }
@@ -96,18 +110,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// 16-byte direct-to-LDS load: lane L's 16 bytes from `src` land at LDS
-// address lds_base + 16 L (lds_base wave-uniform, passed in m0).  Written as
-// asm so that the compiler does not treat every later LDS read as possibly
+// 16-byte direct-to-LDS load: lane L's 16 bytes from `base + off` land at
+// LDS address lds_base + 16 L (lds_base wave-uniform, passed in m0; base a
+// 64-bit scalar address, off the lane's 32-bit byte offset).  Written as asm
+// so that the compiler does not treat every later LDS read as possibly
 // aliasing it (which would make it wait for all loads in flight, prefetches
 // included); completion is tracked explicitly with wait_vmcnt before the
 // barrier that publishes a K step.  The instruction has no result register.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ __forceinline__ void dma16(uint32_t off, const char* base, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds_base)
+               : "v"(off), "s"(base), "s"(lds_base)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -132,61 +147,8 @@ __device__ __forceinline__ void tri_decode(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
-// Within one group's block range (padded to a multiple of 8 and starting at a
-// multiple of 8), block j runs on XCD j % 8 (hardware round-robin); renumber
-// so that XCD x takes the contiguous tile range [x*n/8, (x+1)*n/8): every
-// XCD gets the same share of every group, and consecutive tiles (one
-// matrix's) share an XCD's L2.
-__device__ __forceinline__ int64_t xcd_remap(int64_t j, int64_t npad) {
-#ifdef MUON_NO_XCD_REMAP
-  return j;
-#endif
-  return (j & 7) * (npad >> 3) + (j >> 3);
-}
-
-// One direct-to-LDS instruction of a K-contiguous tile: 16 rows x 64 bytes.
-// Lane L takes row r0 + L/4, physical chunk L%4, i.e. logical chunk
-// (L%4) ^ f(row).
-__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t ld, int k0, int r0,
-                                         uint32_t tile, int lane) {
-  const int row = r0 + (lane >> 2);
-  const int c = (lane & 3) ^ fswz(row);
-  dma16(base + int64_t(row) * ld + k0 + c * 8, tile + r0 * (BK * 2));
-}
-
-// One direct-to-LDS instruction of the update's X tile: 1024/(2 BN) K-rows
-// of 2 BN bytes.  Lane L takes K-row kr0 + L/(BN/8), physical chunk L%(BN/8).
-template <int BN>
-__device__ __forceinline__ void dma_xrows(const uint16_t* base, int64_t ld, int k0, int kr0,
-                                          uint32_t tile, int lane) {
-  constexpr int CPR = BN / 8;  // 16-byte chunks per row
-  const int k = kr0 + lane / CPR;
-  const int c = (lane % CPR) ^ gswz(k);
-  dma16(base + int64_t(k0 + k) * ld + c * 8, tile + kr0 * (BN * 2));
-}
-
 __device__ __forceinline__ bf16x8_t lds_frag_rows(const LDS_AS char* tile, int row, int chunk) {
   return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * (BK * 2) + ((chunk ^ fswz(row)) << 4));
-}
-
-// Four consecutive K-rows at one column of the update's X tile, in the
-// MFMA accumulator's row pattern: lane l (s = l % 16) gets
-// X[kb + 4 (l/32) + j][nb + 16 ((l/16) % 2) + s], j = 0..3 (one transposing
-// read; source lane s addresses X[k + s/4][n + 4 (s%4)]).
-template <int BN>
-__device__ __forceinline__ i16x4_t lds_rows4_xT(const LDS_AS char* tile, int kb, int nb, int lane) {
-  const int s = lane & 15;
-  const int n = nb + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-  const int k = kb + 4 * (lane >> 5) + (s >> 2);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LDS_AS i16x4_t*)(tile + k * (BN * 2) + (((n >> 3) ^ gswz(k)) << 4) + (n & 7) * 2));
-}
-
-// Four consecutive K values (kb + 4 (l/32) .. +3) of row `row` of a
-// K-contiguous tile: one 8-byte read.
-__device__ __forceinline__ i16x4_t lds_k4_rows(const LDS_AS char* tile, int row, int kb, int lane) {
-  const int k = kb + 4 * (lane >> 5);
-  return *(const LDS_AS i16x4_t*)(tile + row * (BK * 2) + (((k >> 3) ^ fswz(row)) << 4) + (k & 7) * 2);
 }
 
 template <int BN>
@@ -203,30 +165,46 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, Work wk, int iter,
-                                                                     float c1, float c2) {
+__global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_kernel(
+    Batch bt, TileList tl, int iter, float c1, float c2) {
   using C = Cfg<MODE>;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES;
+  constexpr int NT = 64 * C::NW;                     // threads per block
   constexpr int A_BYTES = BM * BK * 2;
   constexpr int B_BYTES = BN * BK * 2;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  constexpr int A_INSTR = A_BYTES / WAVE_BYTES / 4;  // per wave
-  constexpr int B_INSTR = B_BYTES / WAVE_BYTES / 4;
+  constexpr int A_INSTR = A_BYTES / WAVE_BYTES / C::NW;  // per wave
+  constexpr int B_INSTR = B_BYTES / WAVE_BYTES / C::NW;
   constexpr int LOADS = A_INSTR + B_INSTR;          // vmcnt per stage per wave
-  static_assert(A_BYTES % (4 * WAVE_BYTES) == 0 && B_BYTES % (4 * WAVE_BYTES) == 0, "tiling");
+  static_assert(A_BYTES % (C::NW * WAVE_BYTES) == 0 && B_BYTES % (C::NW * WAVE_BYTES) == 0, "tiling");
   static_assert((S - 1) * LOADS < 64, "vmcnt field");
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE_BYTES];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
   (void)c2;
 
-  const int64_t bid = blockIdx.x;
-  const int gi = find_group(wk, bid);
+  // Persistent blocks: XCD x (= blockIdx % 8, the hardware's round-robin)
+  // owns the contiguous slice [n x/8, n (x+1)/8) of every group's n tiles,
+  // groups taken in the order of tl.group (longest K first); the
+  // blocks_per_xcd blocks of an XCD walk the concatenated slices with a
+  // stride of blocks_per_xcd, so at any time they hold consecutive tiles (one
+  // matrix's, sharing that XCD's L2).  A block's next tile starts loading
+  // while the stores of its previous tile drain.
+  const int xcd = int(blockIdx.x & 7);
+  const int64_t nbx = tl.blocks_per_xcd;
+  int64_t l = int64_t(blockIdx.x >> 3), base = 0;
+  bool first_tile = true;
+  for (int oi = 0; oi < tl.ngroups; ++oi) {
+  const int64_t lo = tl.n[oi] * xcd / 8, cnt = tl.n[oi] * (xcd + 1) / 8 - lo;
+  const int gi = tl.group[oi];
   const MatGroup& g = bt.g[gi];
-  const int tiles = wk.tiles[gi];
-  const int64_t local = xcd_remap(bid - wk.begin[gi], wk.begin[gi + 1] - wk.begin[gi]);
-  if (local >= g.count * tiles) return;  // padding block
+  const int tiles = tl.tiles[oi];
+  for (; l < base + cnt; l += nbx) {
+  const int64_t local = lo + (l - base);
   const int64_t m = local / tiles;
   const int tile = int(local - m * tiles);
+  // the previous tile's epilogue has finished reading LDS
+  if (!first_tile) block_barrier();
+  first_tile = false;
   int ti, tj;
   if (MODE == MODE_UPDATE) {
     const int ntn = g.q_pad / BN;
@@ -269,31 +247,58 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  static_assert(C::WGM * C::WGN == C::NW && BM % 64 == 0, "wave grid; 64-row epilogue passes");
   const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
 
-  // Issue the loads of K step `kt` into stage buffer kt % S.  Each wave moves
-  // A_INSTR + B_INSTR KiB-sized pieces.
-  auto issue = [&](int kt) {
-    const uint32_t st = smem_base + uint32_t((kt % S) * STAGE_BYTES);
-    const int k0 = kt * BK;
+  // LDS holds the A tiles of all stages, then the B tiles (stage s of A at
+  // s*A_BYTES, of B at S*A_BYTES + s*B_BYTES), so that a lane's address in
+  // any stage is its stage-0 address plus a small compile-time immediate.
+  // DMA sources are a 64-bit scalar base per operand, advanced by one K step
+  // per step, plus a per-lane 32-bit byte offset fixed for the whole tile:
+  // no per-step vector address arithmetic.
+  uint32_t offA[A_INSTR], offB[B_INSTR];
 #pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) dma_rows(Pa, lda, k0, (wave * A_INSTR + i) * 16, st, lane);
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = (wave * A_INSTR + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ fswz(row);
+    offA[i] = uint32_t((int64_t(row) * lda + c * 8) * 2);
+  }
 #pragma unroll
-    for (int i = 0; i < B_INSTR; ++i) {
-      if (MODE == MODE_UPDATE)
-        dma_xrows<BN>(Pb, ldb, k0, (wave * B_INSTR + i) * (1024 / (BN * 2)), st + A_BYTES, lane);
-      else
-        dma_rows(Pb, ldb, k0, (wave * B_INSTR + i) * 16, st + A_BYTES, lane);
+  for (int i = 0; i < B_INSTR; ++i) {
+    if (MODE == MODE_UPDATE) {
+      // K-rows of 2 BN bytes; lane L takes K-row kr0 + L/(BN/8), chunk L%(BN/8)
+      constexpr int CPR = BN / 8;
+      const int k = (wave * B_INSTR + i) * (WAVE_BYTES / (BN * 2)) + lane / CPR;
+      const int c = (lane % CPR) ^ gswz(k);
+      offB[i] = uint32_t((int64_t(k) * ldb + c * 8) * 2);
+    } else {
+      const int row = (wave * B_INSTR + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ fswz(row);
+      offB[i] = uint32_t((int64_t(row) * ldb + c * 8) * 2);
     }
+  }
+  const char* gA = reinterpret_cast<const char*>(Pa);
+  const char* gB = reinterpret_cast<const char*>(Pb);
+  const int64_t stepA = BK * 2;
+  const int64_t stepB = MODE == MODE_UPDATE ? int64_t(BK) * ldb * 2 : int64_t(BK) * 2;
+
+  // Issue the loads of K step `kt` into stage buffer J (= kt % S).  Each wave
+  // moves A_INSTR + B_INSTR KiB-sized pieces.
+  auto issue = [&](auto bufc, int kt) {
+    constexpr int J = decltype(bufc)::value;
+    const char* a = gA + kt * stepA;
+    const char* b = gB + kt * stepB;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i)
+      dma16(offA[i], a, smem_base + uint32_t(J * A_BYTES + (wave * A_INSTR + i) * WAVE_BYTES));
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i)
+      dma16(offB[i], b,
+            smem_base + uint32_t(S * A_BYTES + J * B_BYTES + (wave * B_INSTR + i) * WAVE_BYTES));
   };
 
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-    if (s < nk) issue(s);
-
   f32x16_t acc[WM][WN];
-  float pre[MODE == MODE_POLY ? WM : 1][MODE == MODE_POLY ? WN : 1][16];  // b*A term
 #pragma unroll
   for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
@@ -301,44 +306,11 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  // The a*X term of the update and the b*A term of the polynomial need the
-  // tile's own rows i0 .. i0+127 of X (resp. A, symmetric: A[i][j] =
-  // A[j][i]); those rows pass through LDS as the B operand's K rows of K
-  // steps i0/32 .. i0/32+3.  While K step kt is resident, the wave picks up
-  // the values for its accumulator rows 32 (2 wm + mi) .. +31 when
-  // kt == i0/32 + 2 wm + mi, so the epilogue reads nothing from memory.
-  auto pick_diag = [&](int kt, const LDS_AS char* sB) {
-    if (MODE == MODE_GRAM) return;
-    const int mi = kt - i0 / BK - 2 * wm;
-    if (mi < 0 || mi >= WM) return;
-#pragma unroll
-    for (int m2 = 0; m2 < WM; ++m2) {
-      if (m2 != mi) continue;
-#pragma unroll
-      for (int ni = 0; ni < WN; ++ni)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          i16x4_t v;
-          if (MODE == MODE_UPDATE)
-            v = lds_rows4_xT<BN>(sB, 8 * g4, wn * 32 * WN + ni * 32, lane);
-          else
-            v = lds_k4_rows(sB, wn * 32 * WN + ni * 32 + (lane & 31), 8 * g4, lane);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = __uint_as_float(uint32_t(uint16_t(v[j])) << 16);
-            if (MODE == MODE_UPDATE)
-              acc[m2][ni][4 * g4 + j] = fmaf(c1, x, acc[m2][ni][4 * g4 + j]);
-            else
-              pre[m2][ni][4 * g4 + j] = x;
-          }
-        }
-    }
-  };
-
-  // Fragments of one 16-deep K sub-step of stage buffer `buf`.
-  auto load_frags = [&](int buf, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
-    const LDS_AS char* sA = smem + buf * STAGE_BYTES;
-    const LDS_AS char* sB = sA + A_BYTES;
+  // Fragments of one 16-deep K sub-step of stage buffer J.
+  auto load_frags = [&](auto bufc, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
+    constexpr int J = decltype(bufc)::value;
+    const LDS_AS char* sA = smem + J * A_BYTES;
+    const LDS_AS char* sB = smem + S * A_BYTES + J * B_BYTES;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi) af[mi] = lds_frag_rows(sA, wm * 32 * WM + mi * 32 + (lane & 31), ch);
@@ -371,30 +343,40 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     else
       wait_vmcnt<0>();
   };
-  static_assert(S <= 4, "wait_stage covers at most 3 younger stages");
+  static_assert(S >= 2 && S <= 4, "wait_stage covers at most 3 younger stages");
 
   // Software pipeline over K steps (two 16-deep sub-steps each): the LDS
   // reads of the next sub-step are always in flight while the MFMAs of the
   // current one issue.  One barrier per K step, between its sub-steps: all
   // reads of step kt are complete there (lgkmcnt 0), so its buffer is
   // refilled with step kt+S right after it, and step kt+1 (waited for by
-  // every wave) becomes readable.
+  // every wave) becomes readable.  The loop is unrolled by S so that every
+  // stage buffer index is a compile-time constant.
   bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
+  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, 2);
+  if constexpr (S > 3) if (3 < nk) issue(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, 3);
   wait_stage(0, S - 1);  // the prologue issued steps 0 .. S-1
   block_barrier();
-  load_frags(0, 0, a0, b0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % S;
-    load_frags(buf, 1, a1, b1);
+  load_frags(std::integral_constant<int, 0>{}, 0, a0, b0);
+  auto step = [&](auto bufc, int kt) {
+    constexpr int J = decltype(bufc)::value;
+    load_frags(bufc, 1, a1, b1);
     mfmas(a0, b0);
-    pick_diag(kt, smem + buf * STAGE_BYTES + A_BYTES);
     if (kt + 1 < nk) {
       wait_stage(kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
       block_barrier();
-      if (kt + S < nk) issue(kt + S);
-      load_frags((kt + 1) % S, 0, a0, b0);
+      if (kt + S < nk) issue(bufc, kt + S);
+      load_frags(std::integral_constant<int, (J + 1) % S>{}, 0, a0, b0);
     }
     mfmas(a1, b1);
+  };
+  for (int kt = 0; kt < nk; kt += S) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (S > 2) if (kt + 2 < nk) step(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, kt + 2);
+    if constexpr (S > 3) if (kt + 3 < nk) step(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, kt + 3);
   }
 
   // ---- Epilogue: the final fp32 tile is staged through LDS in two passes
@@ -417,34 +399,32 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MODE == MODE_POLY)
-          acc[mi][ni][r] = fmaf(c2, acc[mi][ni][r], c1 * pre[mi][ni][r]);
-        else
-          acc[mi][ni][r] *= alpha;
-      }
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= (MODE == MODE_POLY ? c2 : alpha);
   constexpr int TP = BN + 8;                 // fp32 staging row pitch (floats)
   static_assert(64 * TP * 4 <= S * STAGE_BYTES, "staging");
   LDS_AS float* T = (LDS_AS float*)smem;
   constexpr int CPR = BN / 8;                // 8-element chunks per row
-  constexpr int CHUNKS = 64 * CPR / 256;     // per thread per pass
+  constexpr int CHUNKS = 64 * CPR / NT;      // per thread per pass
   uint16_t* Cout = MODE == MODE_UPDATE ? Xout : (MODE == MODE_GRAM ? Am : Bm);
   const int64_t ldc = MODE == MODE_UPDATE ? qp : pp;
 
+  // Pass `pass` stages tile rows 64 pass .. +63: the 32-row accumulator
+  // blocks wm*WM + mi with (wm*WM + mi) / 2 == pass.
   auto stage = [&](int pass) {
-    if (wm == pass) {
+#pragma unroll
+    for (int mi = 0; mi < WM; ++mi) {
+      const int blk = wm * WM + mi;
+      if ((blk >> 1) != pass) continue;
       // MFMA 32x32 output layout: lane l, register r holds row
       // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block.
 #pragma unroll
-      for (int mi = 0; mi < WM; ++mi)
+      for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < WN; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int col = wn * 32 * WN + ni * 32 + (lane & 31);
-            T[row * TP + col] = acc[mi][ni][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int row = (blk & 1) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = wn * 32 * WN + ni * 32 + (lane & 31);
+          T[row * TP + col] = acc[mi][ni][r];
+        }
     }
   };
   auto pack8 = [](const float (&v)[8]) {
@@ -453,10 +433,43 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
     for (int e = 0; e < 4; ++e) w[e] = f2bf2(v[2 * e], v[2 * e + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   };
+  // The linear term of the update (alpha*a*X) and of the polynomial (b*A)
+  // at the output positions, read as 16-byte rows of the operand the tile
+  // was computed from (L2-resident: its K steps just streamed through).  A
+  // is symmetric, so a mirrored chunk's term is again a row segment of A.
+  constexpr bool kLin = MODE != MODE_GRAM;
+  constexpr int MCH = BN * 8 / NT;           // mirrored chunks per thread per pass
+  const uint16_t* Lin = MODE == MODE_UPDATE ? Xin : Am;
+  const float lin_coef = MODE == MODE_UPDATE ? alpha * c1 : c1;
+  auto add_lin = [&](float (&v)[8], const uint4& x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = fmaf(lin_coef, __uint_as_float(w[e] << 16), v[2 * e]);
+      v[2 * e + 1] = fmaf(lin_coef, __uint_as_float(w[e] & 0xffff0000u), v[2 * e + 1]);
+    }
+  };
   auto finish = [&](int pass) {
+    uint4 lin[kLin ? CHUNKS : 1], lin_m[kLin ? MCH : 1];
+    if (kLin) {
+#pragma unroll
+      for (int u = 0; u < CHUNKS; ++u) {
+        const int q = t + NT * u;
+        const int row = q / CPR, col = (q % CPR) * 8;
+        lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
+      }
+      if (mirror) {
+#pragma unroll
+        for (int u = 0; u < MCH; ++u) {
+          const int q = t + NT * u;
+          const int c = q % BN, r8 = (q / BN) * 8;
+          lin_m[u] = *reinterpret_cast<const uint4*>(Lin + (j0 + c) * ldc + i0 + 64 * pass + r8);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
-      const int q = t + 256 * u;
+      const int q = t + NT * u;
       const int row = q / CPR, col = (q % CPR) * 8;
       float v[8];
       const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
@@ -466,6 +479,7 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
         v[e] = v0[e];
         v[e + 4] = v1[e];
       }
+      if (kLin) add_lin(v, lin[u]);
       *reinterpret_cast<uint4*>(Cout + (i0 + 64 * pass + row) * ldc + j0 + col) = pack8(v);
     }
     if (mirror) {
@@ -473,41 +487,44 @@ __global__ __launch_bounds__(256, Cfg<MODE>::OCC) void ns_bf16_kernel(Batch bt, 
       // .. +7, from staged column c; lanes take consecutive c, so the
       // column reads hit distinct banks.
 #pragma unroll
-      for (int u = 0; u < BN * 8 / 256; ++u) {
-        const int q = t + 256 * u;
+      for (int u = 0; u < MCH; ++u) {
+        const int q = t + NT * u;
         const int c = q % BN, r8 = (q / BN) * 8;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
+        if (kLin) add_lin(v, lin_m[u]);
         *reinterpret_cast<uint4*>(Cout + (j0 + c) * ldc + i0 + 64 * pass + r8) = pack8(v);
       }
     }
   };
 
-  block_barrier();  // stage buffers no longer read
-  stage(0);
-  block_barrier();
-  finish(0);
-  block_barrier();  // T is rewritten by the next pass
-  stage(1);
-  block_barrier();
-  finish(1);
+#pragma unroll
+  for (int pass = 0; pass < BM / 64; ++pass) {
+    block_barrier();  // stage buffers (pass 0) / the previous pass's T no longer read
+    stage(pass);
+    block_barrier();
+    finish(pass);
+  }
+  }  // tiles of group oi
+  base += cnt;
+  }  // groups
 }
 
-inline dim3 grid_of(const Work& wk) { return dim3(unsigned(wk.begin[wk.ngroups])); }
+inline dim3 grid_of(const TileList& tl) { return dim3(unsigned(8 * tl.blocks_per_xcd)); }
 
 }  // namespace
 
-hipError_t launch_gram_bf16(const Batch& bt, const Work& wk, int iter, hipStream_t s) {
-  hipLaunchKernelGGL(ns_bf16_kernel<MODE_GRAM>, grid_of(wk), dim3(256), 0, s, bt, wk, iter, 0.f, 0.f);
+hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, hipStream_t s) {
+  hipLaunchKernelGGL(ns_bf16_kernel<MODE_GRAM>, grid_of(tl), dim3(64 * Cfg<MODE_GRAM>::NW), 0, s, bt, tl, iter, 0.f, 0.f);
   return hipGetLastError();
 }
-hipError_t launch_poly_bf16(const Batch& bt, const Work& wk, float b, float c, hipStream_t s) {
-  hipLaunchKernelGGL(ns_bf16_kernel<MODE_POLY>, grid_of(wk), dim3(256), 0, s, bt, wk, 0, b, c);
+hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, hipStream_t s) {
+  hipLaunchKernelGGL(ns_bf16_kernel<MODE_POLY>, grid_of(tl), dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, b, c);
   return hipGetLastError();
 }
-hipError_t launch_update_bf16(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s) {
-  hipLaunchKernelGGL(ns_bf16_kernel<MODE_UPDATE>, grid_of(wk), dim3(256), 0, s, bt, wk, iter, a, 0.f);
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, hipStream_t s) {
+  hipLaunchKernelGGL(ns_bf16_kernel<MODE_UPDATE>, grid_of(tl), dim3(64 * Cfg<MODE_UPDATE>::NW), 0, s, bt, tl, iter, a, 0.f);
   return hipGetLastError();
 }
 

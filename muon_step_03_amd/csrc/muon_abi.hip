@@ -204,6 +204,41 @@ int finish_launch(hipError_t e, int phase, hipStream_t s, hipEvent_t t0 = nullpt
   return MUON_OK;
 }
 
+// Compute units per XCD of the current device (0 on a HIP error), cached.
+int cus_per_xcd() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+    return 0;
+  if (dev >= 0 && dev < 64) cache[dev] = n / 8;
+  return n / 8;
+}
+
+// Static tile list of one persistent Newton-Schulz launch: groups with more
+// K steps per tile first (they finish last otherwise), up to the given
+// number of resident blocks per XCD.
+TileList make_tile_list(const Batch& bt, const int64_t* tiles_per_matrix, const int64_t* k_len,
+                        int blocks_per_xcd_max) {
+  TileList tl{};
+  tl.ngroups = bt.ngroups;
+  int order[kMaxGroups];
+  for (int k = 0; k < bt.ngroups; ++k) order[k] = k;
+  std::stable_sort(order, order + bt.ngroups, [&](int a, int b) { return k_len[a] > k_len[b]; });
+  int64_t per_xcd = 0;
+  for (int i = 0; i < bt.ngroups; ++i) {
+    const int k = order[i];
+    tl.group[i] = k;
+    tl.tiles[i] = int(tiles_per_matrix[k]);
+    tl.n[i] = bt.g[k].count * tiles_per_matrix[k];
+    per_xcd += (tl.n[i] + 7) / 8;
+  }
+  tl.blocks_per_xcd = int(std::max<int64_t>(1, std::min<int64_t>(blocks_per_xcd_max, per_xcd)));
+  return tl;
+}
+
 struct Sel {
   const muon_group* g;
   Layout L;
@@ -343,24 +378,38 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       w_upd.tiles[k] = int(pt.update);
       w_tail.tiles[k] = int(pt.tail);
     }
+    TileList tl_gram{}, tl_poly{}, tl_upd{};
+    if (bf16) {
+      const int cpx = cus_per_xcd();
+      if (cpx == 0) {
+        g_last_hip_error = int(hipErrorInvalidDevice);
+        return MUON_ERR_HIP;
+      }
+      int64_t nt[kMaxGroups], nu[kMaxGroups], kq[kMaxGroups], kp[kMaxGroups];
+      for (int k = 0; k < nsel; ++k) {
+        nt[k] = w_gram.tiles[k];
+        nu[k] = w_upd.tiles[k];
+        kq[k] = bt.g[k].q_pad;
+        kp[k] = bt.g[k].p_pad;
+      }
+      tl_gram = make_tile_list(bt, nt, kq, kSyrkBlocksPerCU * cpx);
+      tl_poly = make_tile_list(bt, nt, kp, kSyrkBlocksPerCU * cpx);
+      tl_upd = make_tile_list(bt, nu, kp, kUpdBlocksPerCU * cpx);
+    }
     hipEvent_t t0 = nullptr;
     Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};
     for (Work* w : ws) {
-      // The Newton-Schulz launches pad each group's block range to a
-      // multiple of 8 (one block per XCD slot); padding blocks exit at once.
-      const int64_t pad = (w == &w_gram || w == &w_upd) && bf16 ? 8 : 1;
       w->begin[0] = 0;
-      for (int k = 0; k < nsel; ++k)
-        w->begin[k + 1] = w->begin[k] + (bt.g[k].count * w->tiles[k] + pad - 1) / pad * pad;
+      for (int k = 0; k < nsel; ++k) w->begin[k + 1] = w->begin[k] + bt.g[k].count * w->tiles[k];
     }
 
     if ((t0 = prof_start(s)), (st = finish_launch(launch_head(bt, w_head, bf16, h.momentum, s), 0, s, t0))) return st;
     if ((t0 = prof_start(s)), (st = finish_launch(launch_norm_finalize(bt, w_one, s), 1, s, t0))) return st;
     for (int it = 0; it < ns_steps; ++it) {
       if (bf16) {
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, w_gram, it, s), 2, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, w_upd, it, h.a, s), 4, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram, it, s), 2, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.b, h.c, s), 3, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl_upd, it, h.a, s), 4, s, t0))) return st;
       } else {
         if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_f32(bt, w_gram, it, s), 2, s, t0))) return st;
         if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_f32(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;

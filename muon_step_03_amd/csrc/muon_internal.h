@@ -38,6 +38,14 @@ constexpr int kEwTile = 64;        // head/tail tile edge (elements)
 #ifndef MUON_UPD_TILE_N
 #define MUON_UPD_TILE_N 256
 #endif
+// Waves per update block (4: 128x256 tiles, two blocks per CU; 8: larger
+// tiles, one block per CU).
+#ifndef MUON_UPD_WAVES
+#define MUON_UPD_WAVES 4
+#endif
+constexpr int kUpdWaves = MUON_UPD_WAVES;
+constexpr int kUpdBlocksPerCU = kUpdWaves == 8 ? 1 : 2;
+constexpr int kSyrkBlocksPerCU = 2;
 constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
 constexpr int kUpdTileM = MUON_UPD_TILE_M;  // update: rows (along p)
 constexpr int kUpdTileN = MUON_UPD_TILE_N;  // update: columns (along q)
@@ -99,6 +107,17 @@ struct Work {
   int64_t begin[kMaxGroups + 1];
   int tiles[kMaxGroups];
   int ngroups;
+};
+
+// Static tile list of a persistent Newton-Schulz launch: groups in processing
+// order (longest K first), n[i] tiles (count x tiles per matrix) of group
+// group[i]; 8 * blocks_per_xcd blocks.
+struct TileList {
+  int64_t n[kMaxGroups];
+  int tiles[kMaxGroups];
+  int group[kMaxGroups];
+  int ngroups;
+  int blocks_per_xcd;
 };
 
 struct Hyper {
@@ -210,9 +229,9 @@ hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const H
                              bool reduced, hipStream_t s);
 // Newton-Schulz products.  `iter` selects X0/X1 and the first-iteration norm
 // scaling.
-hipError_t launch_gram_bf16(const Batch& bt, const Work& wk, int iter, hipStream_t s);
-hipError_t launch_poly_bf16(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
-hipError_t launch_update_bf16(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);
+hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, hipStream_t s);
+hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, hipStream_t s);
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, hipStream_t s);
 hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s);
 hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
 hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);

@@ -300,7 +300,10 @@ def main():
             "traffic": measured_traffic(w.name), "avg_launch_ms": avg["update"],
             "alg_flops_per_launch": upd_flops,
         }
-        ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"]
+        # The last update of a step may also apply the step to W (plain Muon
+        # without statistics, bf16): it is timed as its own phase, so
+        # "update" stays the pure GEMM launch of the roofline.
+        ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"] + per_step["update_tail"]
         ns_flops = 5 * (work["gram"] + work["poly"] + work["update"])
         result["ns"] = {"ms_per_step": ns_ms, "tflops": ns_flops / (ns_ms * 1e-3) / 1e12,
                         "frac_of_peak": ns_flops / (ns_ms * 1e-3) / peak,
@@ -309,8 +312,13 @@ def main():
         result["head"] = {"ms": avg["head"], "gbps": work["head_bytes"] / (avg["head"] * 1e-3) / 1e9,
                           "frac_of_hbm": work["head_bytes"] / (avg["head"] * 1e-3) / PEAK_HBM}
         tail_ms = per_step["tail_apply"] + per_step["tail_reduce"] + per_step["tail_finalize"]
-        result["tail"] = {"ms": tail_ms, "gbps": work["tail_bytes"] / (tail_ms * 1e-3) / 1e9,
-                          "frac_of_hbm": work["tail_bytes"] / (tail_ms * 1e-3) / PEAK_HBM}
+        if tail_ms > 0:
+            result["tail"] = {"ms": tail_ms, "gbps": work["tail_bytes"] / (tail_ms * 1e-3) / 1e9,
+                              "frac_of_hbm": work["tail_bytes"] / (tail_ms * 1e-3) / PEAK_HBM}
+        else:
+            result["tail"] = {"ms": 0.0, "fused_into_last_update": True}
+        if per_step["update_tail"] > 0:
+            result["ns"]["last_update_with_step_ms"] = avg["update_tail"]
         result["phase_ms_per_step"] = per_step
 
     if not args.no_aux and args.workload in wl.AUX_SETS:

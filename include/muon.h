@@ -218,11 +218,13 @@ int muon_adamw_step_grouped(const muon_adamw_tensor* tensors, int64_t count, int
  * launches[phase] (arrays of nphases entries, host memory, zeroed by the
  * caller), and forgets the records.  Phases: 0 head, 1 norm_finalize, 2 gram,
  * 3 poly, 4 update, 5 tail_reduce, 6 tail_finalize, 7 tail_apply, 8 adamw
- * (the AdamW entry points).
+ * (the AdamW entry points), 9 update_tail (the last update launch when it
+ * also applies the step, which plain Muon without statistics does on the
+ * bf16 path: then tail_apply covers only the matrices it did not finish).
  * Returns MUON_ERR_INVALID_ARGUMENT for null arrays or nphases < 1, and
  * MUON_ERR_HIP if an event call failed.
  */
-#define MUON_NUM_PHASES 9
+#define MUON_NUM_PHASES 10
 int muon_profile_enable(int enable);
 int muon_profile_read(double* ms_total, int64_t* launches, int nphases);
 /* Static name of a phase ("?" when out of range). */

@@ -37,7 +37,7 @@ EXPORTS = (
     "muon_profile_enable", "muon_profile_read", "muon_phase_name",
     "muon_adamw_step", "muon_adamw_step_grouped",
 )
-MUON_NUM_PHASES = 9
+MUON_NUM_PHASES = 10
 
 
 class MuonGroup(ctypes.Structure):

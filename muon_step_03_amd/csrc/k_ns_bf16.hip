@@ -499,12 +499,91 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
     }
   };
 
+  // Fused tail (last iteration, plain Muon): W' = decay W - step O with O
+  // this tile's final fp32 values, which are never stored.  O is the tile in
+  // short-side-first orientation: O[i][j] is W[i][j], or W[j][i] for a tall
+  // W (trans).  The host enables it only for bf16 weights whose column count
+  // is a multiple of 8, so every 8-element chunk along W's rows is entirely
+  // inside or outside the matrix.
+  const bool fuse = MODE == MODE_UPDATE && tl.fuse_tail && g.fuse;
+  // W' = decay W + (-step) O for one 8-element chunk of W at wp (16-byte
+  // access when W is 16-byte aligned, element by element otherwise).
+  auto w_update = [&](uint16_t* wp, bool wvec, const float (&o)[8]) {
+    const float dec = g.decay, stp = g.step;
+    float v[8];
+    if (wvec) {
+      const uint4 w = *reinterpret_cast<const uint4*>(wp);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = fmaf(dec, __uint_as_float(ww[e] << 16), -stp * o[2 * e]);
+        v[2 * e + 1] = fmaf(dec, __uint_as_float(ww[e] & 0xffff0000u), -stp * o[2 * e + 1]);
+      }
+      *reinterpret_cast<uint4*>(wp) = pack8(v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wp[e] = f2bf(fmaf(dec, bf2f(wp[e]), -stp * o[e]));
+    }
+  };
+  auto finish_tail = [&](int pass) {
+    uint16_t* Wm = mat_ptr<uint16_t>(g.W_tab, g.W, m, int64_t(g.rows) * g.cols);
+    const int64_t wld = g.cols;
+    const bool wvec = (reinterpret_cast<uintptr_t>(Wm) & 15) == 0;
+    uint4 lin[CHUNKS];
+#pragma unroll
+    for (int u = 0; u < CHUNKS; ++u) {
+      const int q = t + NT * u;
+      const int row = q / CPR, col = (q % CPR) * 8;
+      lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
+    }
+#pragma unroll
+    for (int u = 0; u < CHUNKS; ++u) {
+      const int q = t + NT * u;
+      const int row = q / CPR, col = (q % CPR) * 8;
+      float v[8];
+      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
+      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = v0[e];
+        v[e + 4] = v1[e];
+      }
+      add_lin(v, lin[u]);
+      const int i = i0 + 64 * pass + row, j = j0 + col;
+      if (!g.trans) {
+        if (i < g.p && j < g.q) w_update(Wm + int64_t(i) * wld + j, wvec, v);
+      } else {
+        // O is needed by columns: keep the complete values in T
+        *(LDS_AS f32x4_t*)(T + row * TP + col) = f32x4_t{v[0], v[1], v[2], v[3]};
+        *(LDS_AS f32x4_t*)(T + row * TP + col + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+      }
+    }
+    if (g.trans) {
+      block_barrier();
+      // W row j0 + c, columns i0 + 64 pass + r8 .. +7, from staged column c
+#pragma unroll
+      for (int u = 0; u < BN * 8 / NT; ++u) {
+        const int q = t + NT * u;
+        const int c = q % BN, r8 = (q / BN) * 8;
+        const int i = i0 + 64 * pass + r8, j = j0 + c;
+        if (j >= g.q || i >= g.p) continue;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
+        w_update(Wm + int64_t(j) * wld + i, wvec, v);
+      }
+    }
+  };
+
 #pragma unroll
   for (int pass = 0; pass < BM / 64; ++pass) {
     block_barrier();  // stage buffers (pass 0) / the previous pass's T no longer read
     stage(pass);
     block_barrier();
-    finish(pass);
+    if (fuse)
+      finish_tail(pass);
+    else
+      finish(pass);
   }
   }  // tiles of group oi
   base += cnt;

@@ -142,10 +142,11 @@ PhaseTiles phase_tiles(const Layout& L, bool bf16) {
 }
 
 const char* kPhaseNames[] = {"head",        "norm_finalize", "gram",       "poly",  "update",
-                             "tail_reduce", "tail_finalize", "tail_apply", "adamw"};
+                             "tail_reduce", "tail_finalize", "tail_apply", "adamw", "update_tail"};
 static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == MUON_NUM_PHASES,
               "one name per phase");
 constexpr int kPhaseAdamw = 8;
+constexpr int kPhaseUpdateTail = 9;  // last update launch with the step fused in
 
 // ---- optional phase timing (HIP events around each launch)
 struct ProfRecord {
@@ -370,14 +371,20 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       const double sfac = keller ? std::sqrt(std::max(1.0, double(u.rows) / double(u.cols)))
                                  : 0.2 * std::sqrt(double(L.q));
       m.step = float(lr * sfac);
+      // Plain Muon without statistics needs no reduction over the finished O,
+      // so the last Newton-Schulz update applies the step to W itself (bf16
+      // weights whose row length allows whole 16-byte chunks).
+      m.fuse = (bf16 && !reduce && ns_steps >= 1 && (u.cols % 8) == 0) ? 1 : 0;
 
       const PhaseTiles pt = phase_tiles(L, dtype == MUON_DTYPE_BF16);
       w_head.tiles[k] = int(pt.head);
       w_one.tiles[k] = 1;
       w_gram.tiles[k] = int(pt.gram);
       w_upd.tiles[k] = int(pt.update);
-      w_tail.tiles[k] = int(pt.tail);
+      w_tail.tiles[k] = m.fuse ? 0 : int(pt.tail);
     }
+    bool any_fused = false;
+    for (int k = 0; k < nsel; ++k) any_fused = any_fused || bt.g[k].fuse;
     TileList tl_gram{}, tl_poly{}, tl_upd{};
     if (bf16) {
       const int cpx = cus_per_xcd();
@@ -409,7 +416,10 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       if (bf16) {
         if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram, it, s), 2, s, t0))) return st;
         if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.b, h.c, s), 3, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl_upd, it, h.a, s), 4, s, t0))) return st;
+        TileList tl = tl_upd;
+        tl.fuse_tail = (it == ns_steps - 1 && any_fused) ? 1 : 0;
+        const int ph = tl.fuse_tail ? kPhaseUpdateTail : 4;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, h.a, s), ph, s, t0))) return st;
       } else {
         if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_f32(bt, w_gram, it, s), 2, s, t0))) return st;
         if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_f32(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;
@@ -420,8 +430,9 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, s), 5, s, t0))) return st;
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, s), 6, s, t0))) return st;
     }
-    if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),
-                                                   7, s, t0)))
+    if (w_tail.begin[nsel] > 0 &&  // every group may have been finished by its last update
+        ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),
+                                                    7, s, t0))))
       return st;
   }
   return MUON_OK;

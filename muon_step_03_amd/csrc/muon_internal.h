@@ -94,6 +94,7 @@ struct MatGroup {
   float* stats;        // MUON_STATS_PER_MATRIX per matrix, or null
   float decay;         // 1 - lr*wd
   float step;          // lr * s, s = 0.2*sqrt(max(rows, cols)) or max(1, rows/cols)^0.5
+  int fuse;            // 1: the last update applies W' = decay W - step O itself
 };
 
 struct Batch {
@@ -118,6 +119,8 @@ struct TileList {
   int group[kMaxGroups];
   int ngroups;
   int blocks_per_xcd;
+  int fuse_tail;   // update launch of the last iteration: groups with fuse set
+                   // write W' instead of X'
 };
 
 struct Hyper {

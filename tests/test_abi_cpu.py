@@ -172,8 +172,8 @@ def test_grouped_validation(L):
 def test_phase_names_and_profile_args(L):
     names = [L.muon_phase_name(i).decode() for i in range(_lib.MUON_NUM_PHASES)]
     assert names == ["head", "norm_finalize", "gram", "poly", "update", "tail_reduce",
-                     "tail_finalize", "tail_apply", "adamw"]
-    assert L.muon_phase_name(9) == b"?" and L.muon_phase_name(-1) == b"?"
+                     "tail_finalize", "tail_apply", "adamw", "update_tail"]
+    assert L.muon_phase_name(10) == b"?" and L.muon_phase_name(-1) == b"?"
     assert L.muon_profile_read(None, None, 8) == 1
     ms = (ctypes.c_double * 8)()
     n = (ctypes.c_int64 * 8)()

@@ -15,8 +15,8 @@ import oracle
 from muon_step_03_amd import (MuonError, MuonStep, muon_step, muon_step_batched,
                               muon_step_grouped, stacked_group)
 from muon_step_03_amd import workloads as wl
-from _parity import (HP, TOL_BF16, TOL_F32, check_against_oracle, check_bf16_elementwise,
-                     check_muongs_invariants, f64, oracle_step, relF)
+from _parity import (HP, TOL_BF16, TOL_F32, TOL_M, bf16_round, check_against_oracle,
+                     check_bf16_elementwise, check_muongs_invariants, f64, oracle_step, relF)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -79,6 +79,56 @@ def test_bf16_ragged(shape, variant):
     W1, M1, st = gpu_step(W, G, M, variant=variant)
     e, _, _ = check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st)
     print(f"bf16 {shape} {variant}: relF(dW) = {e:.2e}")
+
+
+# Plain Muon without statistics: on the bf16 path the last Newton-Schulz
+# update applies the step to W itself whenever the weight's row length is a
+# multiple of 8 (the other shapes here take the separate tail).
+FUSED_SHAPES = [(256, 512), (512, 256), (200, 304), (304, 200), (1000, 64), (64, 1000),
+                (257, 129), (129, 257), (8, 8), (384, 384)]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES)
+@pytest.mark.parametrize("ns", [1, 5])
+def test_bf16_without_stats(shape, ns):
+    """The step applied by the last update (no statistics) against the oracle
+    and against the separate tail (statistics requested) on the same inputs.
+    One iteration leaves ||O|| near 3.4 instead of near sqrt(p): the bf16
+    update is then a few bf16 spacings of W, so the bar adds what rounding
+    the exact W' to bf16 costs.  On an 8x8 matrix the relative error of 64
+    elements can exceed the bar on both paths alike: there the fused result
+    must be no worse than the separate one."""
+    W, G, M = inputs(*shape, torch.bfloat16, seed=hash(shape) % 10000 + ns, m_std=1e-3)
+    W1, M1, _ = gpu_step(W, G, M, stats=False, ns_steps=ns)
+    W2, M2, _ = gpu_step(W, G, M, stats=True, ns_steps=ns)
+    assert torch.equal(M1, M2)
+    Wr, Mr, _ = oracle_step(W, G, M, ns_steps=ns)
+    w0 = f64(W)
+    e_f = relF(f64(W1) - w0, Wr - w0)
+    e_s = relF(f64(W2) - w0, Wr - w0)
+    tol = TOL_BF16
+    if ns == 1:
+        tol += relF(bf16_round(Wr), Wr) * float(np.linalg.norm(Wr) / np.linalg.norm(Wr - w0))
+    print(f"bf16 {shape} ns={ns}: relF(dW) fused {e_f:.2e}, separate tail {e_s:.2e}")
+    assert e_f <= tol or (min(shape) < 32 and e_f <= 1.1 * e_s), (e_f, e_s, tol)
+    assert relF(f64(M1), Mr) <= TOL_M
+
+
+def test_fused_and_separate_tail_agree():
+    """The same step with statistics (separate tail, O rounded to bf16 first)
+    and without (step applied in the last update from fp32 O): both meet the
+    bar, and they differ by no more than the bf16 rounding of O can move W'."""
+    shape = (768, 3072)
+    W, G, M = inputs(*shape, torch.bfloat16, seed=91, m_std=1e-3)
+    Wf, Mf, _ = gpu_step(W, G, M, stats=False)
+    Ws, Ms, st = gpu_step(W, G, M, stats=True)
+    check_against_oracle(W, G, M, Wf, Mf)
+    check_against_oracle(W, G, M, Ws, Ms, stats=st)
+    assert torch.equal(Mf, Ms)
+    step = 0.02 * 0.2 * math.sqrt(max(shape))
+    O_bound = 2.0 ** -8 * 1.25 * step        # |O| <= ~1.2: half a bf16 ulp of O, scaled
+    w_ulp = 2.0 ** -7 * np.maximum(np.abs(f64(Wf)), np.abs(f64(Ws)))
+    assert np.all(np.abs(f64(Wf) - f64(Ws)) <= O_bound + w_ulp)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -275,15 +325,17 @@ def sampled(w, per_group=2):
     return out
 
 
-@pytest.mark.parametrize("variant", ["muon", "muongs"])
-def test_gpt160m_full_set(variant):
+@pytest.mark.parametrize("variant,with_stats", [("muon", True), ("muongs", True), ("muon", False)])
+def test_gpt160m_full_set(variant, with_stats):
+    """The grouped launch the benchmark times (without statistics: the step
+    is applied by the last update), and with per-matrix statistics."""
     w = wl.WORKLOADS["gpt160m"]
     Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
-    stats = torch.zeros(w.n_matrices * 5, device=DEV)
+    stats = torch.zeros(w.n_matrices * 5, device=DEV) if with_stats else None
     W0, Gs, M0 = run_workload(w, 0, Ws, Ms, variant, stats)
     base = np.cumsum([0] + [g.count for g in w.groups])
     for gi, i in sampled(w):
-        st = stats[(base[gi] + i) * 5:(base[gi] + i + 1) * 5]
+        st = stats[(base[gi] + i) * 5:(base[gi] + i + 1) * 5] if with_stats else None
         e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i], Ms[gi][i],
                                        variant=variant, stats=st)
         print(f"gpt160m {w.groups[gi]} #{i} {variant}: relF(dW) = {e:.2e}")

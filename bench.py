@@ -292,7 +292,14 @@ def main():
         avg = {L.muon_phase_name(i).decode(): (ms[i] / cnt[i] if cnt[i] else 0.0) for i in range(n)}
         per_step = {L.muon_phase_name(i).decode(): ms[i] / args.steps for i in range(n)}
         peak = PEAK_MFMA[w.dtype]
-        upd_flops = work["update"]
+        # Algorithmic flops per "update" launch: the update work of every
+        # iteration timed in this phase (the last one is timed apart when it
+        # also applies the step), spread over its launches (two per
+        # iteration when the library runs two chains).
+        per = {k: cnt[i] / args.steps for i, k in enumerate(
+            L.muon_phase_name(i).decode() for i in range(n))}
+        upd_iters = HP["ns_steps"] - (1 if per["update_tail"] > 0 else 0)
+        upd_flops = work["update"] * upd_iters / per["update"]
         a = upd_flops / (avg["update"] * 1e-3)
         result["roofline"] = {
             "kernel": "ns_update (X' = aX + B X)", "bound": "mfma",

@@ -21,6 +21,8 @@ named after the key):
        (blog.pieroot.xyz), section "2. Key Methods and Approach".
   [MX] "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저"
        (codersblog.github.io).
+  [ME] "행과 열을 함께 정규화하는 사전학습 옵티마이저 MeqMuon 공개"
+       (ailog.hnlab.kr), section "핵심 내용".
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes of the repository):
@@ -38,7 +40,10 @@ the design notes of the repository):
     is the identity.  Weight decay, when non-zero, is applied in every variant.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
-(closed forms, invariants, library special cases); none is "parity unpinned".
+(closed forms, invariants, library special cases), except the direction
+MeqMuon chooses (``meqmuon_direction``): the page gives no rule, so that
+choice is "parity unpinned" (the two normalisations it chooses between are
+pinned).
 """
 from __future__ import annotations
 
@@ -62,6 +67,8 @@ RMS_MATCH = 0.2
 VARIANT_MUON = "muon"
 VARIANT_MUONGS = "muongs"
 VARIANT_MUONH = "muonh"
+VARIANT_NORMUON = "normuon"
+VARIANT_MEQMUON = "meqmuon"
 SCALE_MOONLIGHT = "moonlight"
 SCALE_KELLER = "keller"
 
@@ -160,6 +167,46 @@ def muonh_renormalise(W, W_hat):
     return W_hat * (R / n) if n > 0 else W_hat
 
 
+def _equalise(O, axis):
+    """Every row (axis=1: norms taken along each row) or column (axis=0) of
+    O rescaled to the mean norm ||O||_F / sqrt(count); zero ones stay zero."""
+    O = _f64(O)
+    norms = np.sqrt(np.sum(O * O, axis=axis, keepdims=True))
+    count = O.shape[1 - axis]
+    target = np.sqrt(frobenius_inner(O, O) / count)
+    scale = np.divide(target, norms, out=np.zeros_like(norms), where=norms > 0)
+    return O * scale
+
+
+def normuon_rows(O):
+    """[ME] "핵심 내용": NorMuon normalises the size of the orthogonalised
+    update row by row.  Reading (the page prints no formula): each row of O
+    gets the mean row norm ||O||_F / sqrt(rows), so ||O||_F is kept."""
+    return _equalise(O, axis=1)
+
+
+def normuon_cols(O):
+    """The same along columns (MeqMuon's other direction, [ME])."""
+    return _equalise(O, axis=0)
+
+
+def _spread(norms):
+    """Coefficient of variation (std / mean) of a set of norms (0 if all 0)."""
+    mean = float(np.mean(norms))
+    return float(np.std(norms)) / mean if mean > 0 else 0.0
+
+
+def meqmuon_direction(O):
+    """[ME]: MeqMuon picks row or column normalisation per matrix by itself.
+    Reading (no rule on the page; parity unpinned for this choice): the
+    direction whose norms are more spread out (larger std / mean) is
+    equalised; ties go to rows."""
+    O = _f64(O)
+    rn = np.sqrt(np.sum(O * O, axis=1))
+    cn = np.sqrt(np.sum(O * O, axis=0))
+    return "rows" if _spread(rn) >= _spread(cn) else "cols"
+
+
 def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
               weight_decay=DEFAULT_WEIGHT_DECAY, ns_steps=DEFAULT_NS_STEPS,
               a=NS_COEFFICIENTS[0], b=NS_COEFFICIENTS[1], c=NS_COEFFICIENTS[2],
@@ -174,6 +221,7 @@ def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
         M'  = mu M + G;  U = G + mu M'
         O   = NS_{a,b,c}^{ns_steps}(U)
         O~  = O - (<W,O>/||W||^2) W        (MuonGS only)
+        O~  = rows (or columns) of O at equal norm   (NorMuon, MeqMuon)
         s   = 0.2 sqrt(max(A, B))           (or Keller's max(1, A/B)^0.5)
         W'  = (1 - lr*wd) W - lr * s * O~
         W'  = ||W|| W' / ||W'||             (MuonH only)
@@ -190,13 +238,21 @@ def muon_step(W, G, M, *, lr=DEFAULT_LR, momentum=DEFAULT_MOMENTUM,
         raise ValueError("Muon updates 2-D weight matrices only")
     if G.shape != W.shape or M.shape != W.shape:
         raise ValueError("W, G and M must have the same shape")
-    if variant not in (VARIANT_MUON, VARIANT_MUONGS, VARIANT_MUONH):
+    if variant not in (VARIANT_MUON, VARIANT_MUONGS, VARIANT_MUONH, VARIANT_NORMUON,
+                       VARIANT_MEQMUON):
         raise ValueError(f"unknown variant {variant!r}")
     rows, cols = W.shape
 
     M_new, U = nesterov_momentum(G, M, momentum)
     O = newton_schulz(U, a, b, c, ns_steps, eps)
-    O_t = muongs_project(W, O) if variant == VARIANT_MUONGS else O
+    if variant == VARIANT_MUONGS:
+        O_t = muongs_project(W, O)
+    elif variant == VARIANT_NORMUON:
+        O_t = normuon_rows(O)
+    elif variant == VARIANT_MEQMUON:
+        O_t = normuon_rows(O) if meqmuon_direction(O) == "rows" else normuon_cols(O)
+    else:
+        O_t = O
     s = update_scale(rows, cols, scale)
     W_new = (1.0 - lr * weight_decay) * W - lr * s * O_t
     if variant == VARIANT_MUONH:

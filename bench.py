@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt160m")
-    ap.add_argument("--variant", default="muon", choices=["muon", "muongs", "muonh"])
+    ap.add_argument("--variant", default="muon", choices=["muon", "muongs", "muonh", "normuon", "meqmuon"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -47,9 +47,11 @@
  *           on entry are ignored and are garbage on exit.
  *  Stats    optional device float array, MUON_STATS_PER_MATRIX floats per
  *           matrix (matrix order: group by group, then index within the
- *           group): ||U||_F, ||W||_F^2, <W,O>_F, ||O||_F^2, ||O~||_F^2 (= ||O||^2
- *           unless MuonGS), all computed in float32 on the GPU (W and O before
- *           the update).  NULL skips them.
+ *           group): ||U||_F, ||W||_F^2, <W,O>_F, ||O||_F^2, ||O~||_F^2 (the
+ *           projected O for MuonGS, the equalised O for NorMuon/MeqMuon,
+ *           ||O||^2 otherwise), all computed in float32 on the GPU (W and O
+ *           before the update).
+ *           NULL skips them.
  *  Stream   a hipStream_t passed as void*; NULL is the default stream.  The
  *           call only enqueues work: it does not synchronise, allocate device
  *           memory or copy to the host.  Kernel faults surface at the
@@ -94,11 +96,26 @@ enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 };
  *   MUON_VARIANT_MUONH   fixed-radius control (the MuonH the MuonGS page
  *                        compares against): W' = ||W||_F * W^ / ||W^||_F with
  *                        W^ = (1 - lr*wd) W - lr*s*O, so ||W||_F never changes;
+ *   MUON_VARIANT_NORMUON every row of O (weight orientation) rescaled to the
+ *                        mean row norm ||O||_F / sqrt(rows), zero rows kept
+ *                        zero ("행과 열을 함께 정규화하는 사전학습 옵티마이저
+ *                        MeqMuon 공개" (ailog.hnlab.kr), "핵심 내용": NorMuon
+ *                        normalises the update row by row);
+ *   MUON_VARIANT_MEQMUON the same along rows or along columns, whichever set
+ *                        of norms has the larger std/mean (ties: rows) — the
+ *                        same page: MeqMuon chooses the direction by itself;
+ *                        the rule is this library's reading;
  * optionally OR-ed with MUON_SCALE_KELLER to use Keller's shape factor
  * s = max(1, rows/cols)^0.5 (last line of the loss-spike page's Newton-Schulz
  * code block) instead of Moonlight's 0.2*sqrt(max(rows, cols)).
  */
-enum { MUON_VARIANT_MUON = 0, MUON_VARIANT_MUONGS = 1, MUON_VARIANT_MUONH = 2 };
+enum {
+  MUON_VARIANT_MUON = 0,
+  MUON_VARIANT_MUONGS = 1,
+  MUON_VARIANT_MUONH = 2,
+  MUON_VARIANT_NORMUON = 3,
+  MUON_VARIANT_MEQMUON = 4
+};
 #define MUON_SCALE_KELLER 0x100
 
 #define MUON_STATS_PER_MATRIX 5

@@ -22,6 +22,8 @@ MUON_DTYPE_BF16 = 1
 MUON_VARIANT_MUON = 0
 MUON_VARIANT_MUONGS = 1
 MUON_VARIANT_MUONH = 2
+MUON_VARIANT_NORMUON = 3
+MUON_VARIANT_MEQMUON = 4
 MUON_SCALE_KELLER = 0x100
 MUON_STATS_PER_MATRIX = 5
 MUON_MAX_DIM = 32768

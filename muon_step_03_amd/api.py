@@ -22,7 +22,8 @@ from . import _lib
 
 NS_COEFFICIENTS = (3.4445, -4.7750, 2.0315)
 VARIANTS = {"muon": _lib.MUON_VARIANT_MUON, "muongs": _lib.MUON_VARIANT_MUONGS,
-            "muonh": _lib.MUON_VARIANT_MUONH}
+            "muonh": _lib.MUON_VARIANT_MUONH, "normuon": _lib.MUON_VARIANT_NORMUON,
+            "meqmuon": _lib.MUON_VARIANT_MEQMUON}
 SCALES = {"moonlight": 0, "keller": _lib.MUON_SCALE_KELLER}
 _DTYPES = {torch.float32: _lib.MUON_DTYPE_F32, torch.bfloat16: _lib.MUON_DTYPE_BF16}
 

@@ -242,7 +242,7 @@ __device__ __forceinline__ void load_w_tile(const MatGroup& g, const typename El
 // Per-tile partials of <W,O>, ||W||^2, ||O||^2 (O scaled by 1/(||U||+eps)
 // when no Newton-Schulz step ran, since X0 holds the unnormalised U).
 template <bool BF16>
-__global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int ns_steps) {
+__global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int ns_steps, int rc) {
   using TE = typename Elem<BF16>::T;
   __shared__ float S[T][T + 1];
   __shared__ float red[4];
@@ -279,6 +279,109 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
     p[1] = ww;
     p[2] = oo;
   }
+  if (rc) {
+    // Row and column sums of O^2 over this tile: 64 + 64 partials.  A row's
+    // 64 values sit in 16 consecutive threads (shuffle reduction); a
+    // column's in the 16 row groups (through LDS).
+    const int t = threadIdx.x;
+    const int rb = t >> 4, cq = (t & 15) * 4;
+    float* out = g.rc_part + (tr.m * g.tail_tiles + tr.tile) * (2 * T);
+    float rs[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      rs[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ov = valid[k][e] ? o[k][e] * oscale : 0.f;
+        rs[k] = fmaf(ov, ov, rs[k]);
+        cs[e] = fmaf(ov, ov, cs[e]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) rs[k] += __shfl_xor(rs[k], off, 16);
+    if ((t & 15) == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[rb + 16 * k] = rs[k];
+    }
+    __syncthreads();  // S is free again (load_o_tile may have used it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[rb][cq + e] = cs[e];
+    __syncthreads();
+    if (t < T) {
+      float c = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c += S[r][t];
+      out[T + t] = c;
+    }
+  }
+}
+
+// NorMuon / MeqMuon, one block per matrix: squared row and column norms of O
+// from the tile partials, the direction to equalise (NorMuon: rows; MeqMuon:
+// the one whose norms have the larger std/mean, rows on a tie), and the
+// scales target/norm along it (target = ||O||_F / sqrt(count), 0 for a zero
+// row or column) and 1 along the other.
+__global__ __launch_bounds__(256) void rc_finalize_kernel(Batch bt, Work wk, int variant) {
+  __shared__ float red[4];
+  const TileRef tr = decode(bt, wk);
+  const MatGroup& g = *tr.g;
+  const int tcn = g.tail_tiles_c, trn = g.tail_tiles / g.tail_tiles_c;
+  const float* part = g.rc_part + tr.m * g.tail_tiles * (2 * T);
+  float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
+  float* scol = srow + g.rows;
+  float sum_r = 0.f, sum_c = 0.f, s2 = 0.f;
+  for (int r = threadIdx.x; r < g.rows; r += 256) {
+    const int ti = r / T, ri = r - ti * T;
+    float a = 0.f;
+    for (int tc = 0; tc < tcn; ++tc) a += part[(ti * tcn + tc) * (2 * T) + ri];
+    srow[r] = a;
+    sum_r += sqrtf(a);
+    s2 += a;
+  }
+  for (int c = threadIdx.x; c < g.cols; c += 256) {
+    const int tc = c / T, ci = c - tc * T;
+    float a = 0.f;
+    for (int ti = 0; ti < trn; ++ti) a += part[(ti * tcn + tc) * (2 * T) + T + ci];
+    scol[c] = a;
+    sum_c += sqrtf(a);
+  }
+  sum_r = block_sum_256(sum_r, red);
+  sum_c = block_sum_256(sum_c, red);
+  s2 = block_sum_256(s2, red);
+  // std/mean of the norms from a second pass over (norm - mean)^2 (the
+  // one-pass E[x^2]/E[x]^2 - 1 cancels badly for nearly equal norms)
+  const float mean_r = sum_r / float(g.rows), mean_c = sum_c / float(g.cols);
+  float dev_r = 0.f, dev_c = 0.f;
+  for (int r = threadIdx.x; r < g.rows; r += 256) {
+    const float d = sqrtf(srow[r]) - mean_r;
+    dev_r = fmaf(d, d, dev_r);
+  }
+  for (int c = threadIdx.x; c < g.cols; c += 256) {
+    const float d = sqrtf(scol[c]) - mean_c;
+    dev_c = fmaf(d, d, dev_c);
+  }
+  dev_r = block_sum_256(dev_r, red);
+  dev_c = block_sum_256(dev_c, red);
+  const float spread_r = mean_r > 0.f ? sqrtf(dev_r / float(g.rows)) / mean_r : 0.f;
+  const float spread_c = mean_c > 0.f ? sqrtf(dev_c / float(g.cols)) / mean_c : 0.f;
+  const bool rows_dir = variant == MUON_VARIANT_NORMUON || spread_r >= spread_c;
+  const int n = rows_dir ? g.rows : g.cols;
+  const float target = sqrtf(s2 / float(n));
+  float nnz = 0.f;
+  for (int r = threadIdx.x; r < g.rows; r += 256) {
+    const float a = srow[r];
+    if (rows_dir && a > 0.f) nnz += 1.f;
+    srow[r] = rows_dir ? (a > 0.f ? target / sqrtf(a) : 0.f) : 1.f;
+  }
+  for (int c = threadIdx.x; c < g.cols; c += 256) {
+    const float a = scol[c];
+    if (!rows_dir && a > 0.f) nnz += 1.f;
+    scol[c] = rows_dir ? 1.f : (a > 0.f ? target / sqrtf(a) : 0.f);
+  }
+  nnz = block_sum_256(nnz, red);
+  if (threadIdx.x == 0 && g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 4] = target * target * nnz;
 }
 
 // Per-matrix totals: ||W||^2, <W,O>, ||O||^2, the MuonGS coefficient and the
@@ -326,7 +429,7 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
 // coefficient, h the MuonH renormalisation (coef = 0, h = 1 for plain Muon).
 template <bool BF16>
 __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int ns_steps,
-                                                         int reduced) {
+                                                         int reduced, int rc) {
   using E = Elem<BF16>;
   using TE = typename E::T;
   __shared__ float S[T][T + 1];
@@ -353,6 +456,16 @@ __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int 
 
   const int t = threadIdx.x;
   const int rb = t >> 4, cq = (t & 15) * 4;
+  if (rc) {
+    // NorMuon / MeqMuon: O scaled per row and per column (one of the two is 1)
+    const float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
+    const float* scol = srow + g.rows;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid[k][e]) o[k][e] *= srow[r0 + rb + 16 * k] * scol[c0 + cq + e];
+  }
   const bool vec = (c0 + T <= g.cols) && ((g.cols & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(W) & (BF16 ? 7u : 15u)) == 0);
 #pragma unroll
@@ -390,12 +503,12 @@ hipError_t launch_norm_finalize(const Batch& bt, const Work& wk, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps,
+hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps, bool rc,
                               hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL(tail_reduce_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, ns_steps);
+    hipLaunchKernelGGL(tail_reduce_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, ns_steps, int(rc));
   else
-    hipLaunchKernelGGL(tail_reduce_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, ns_steps);
+    hipLaunchKernelGGL(tail_reduce_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, ns_steps, int(rc));
   return hipGetLastError();
 }
 
@@ -404,14 +517,20 @@ hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hi
   return hipGetLastError();
 }
 
+hipError_t launch_rc_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s) {
+  hipLaunchKernelGGL(rc_finalize_kernel, grid_of(wk), dim3(256), 0, s, bt, wk, variant);
+  return hipGetLastError();
+}
+
 hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,
                              bool reduced, hipStream_t s) {
+  const int rc = (h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON) ? 1 : 0;
   if (bf16)
     hipLaunchKernelGGL(tail_apply_kernel<true>, grid_of(wk), dim3(256), 0, s, bt, wk, h.ns_steps,
-                       int(reduced));
+                       int(reduced), rc);
   else
     hipLaunchKernelGGL(tail_apply_kernel<false>, grid_of(wk), dim3(256), 0, s, bt, wk, h.ns_steps,
-                       int(reduced));
+                       int(reduced), rc);
   return hipGetLastError();
 }
 

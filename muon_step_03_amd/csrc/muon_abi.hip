@@ -55,6 +55,7 @@ struct Layout {
   int64_t tile;             // NS GEMM block tile edge along p
   int64_t tile_n;           // update GEMM block tile edge along q
   size_t x_bytes, a_bytes, head_bytes, tail_bytes, scal_bytes;
+  size_t rc_bytes, rcs_bytes;  // row/column partials and scales (NorMuon, MeqMuon)
   size_t total;             // 0 on overflow
 };
 
@@ -77,12 +78,19 @@ Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
       !mul_ok(c, size_t(L.head_tiles) * 4, &h) || !mul_ok(c, size_t(L.tail_tiles) * 12, &t) ||
       !mul_ok(c, size_t(kScal) * 4, &s))
     return L;  // total stays 0
+  size_t rc, rcs;
+  if (!mul_ok(c, size_t(L.tail_tiles) * 2 * kEwTile * 4, &rc) ||
+      !mul_ok(c, size_t(rows + cols) * 4, &rcs))
+    return L;
   L.x_bytes = align_up(x);
   L.a_bytes = align_up(a);
   L.head_bytes = align_up(h);
   L.tail_bytes = align_up(t);
   L.scal_bytes = align_up(s);
-  L.total = 2 * L.x_bytes + 2 * L.a_bytes + L.head_bytes + L.tail_bytes + L.scal_bytes;
+  L.rc_bytes = align_up(rc);
+  L.rcs_bytes = align_up(rcs);
+  L.total = 2 * L.x_bytes + 2 * L.a_bytes + L.head_bytes + L.tail_bytes + L.scal_bytes +
+            L.rc_bytes + L.rcs_bytes;
   if (L.total < L.x_bytes) L.total = 0;
   return L;
 }
@@ -94,8 +102,8 @@ int check_scalars(double lr, double momentum, double wd, int ns_steps, double a,
     return MUON_ERR_INVALID_ARGUMENT;
   if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS) return MUON_ERR_INVALID_ARGUMENT;
   const int base = variant & 0xff;
-  if ((variant & ~(0xff | MUON_SCALE_KELLER)) != 0 ||
-      (base != MUON_VARIANT_MUON && base != MUON_VARIANT_MUONGS && base != MUON_VARIANT_MUONH))
+  if ((variant & ~(0xff | MUON_SCALE_KELLER)) != 0 || base < MUON_VARIANT_MUON ||
+      base > MUON_VARIANT_MEQMUON)
     return MUON_ERR_INVALID_ARGUMENT;
   return MUON_OK;
 }
@@ -364,6 +372,10 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       base += L.tail_bytes;
       m.scal = reinterpret_cast<float*>(base);
       base += L.scal_bytes;
+      m.rc_part = reinterpret_cast<float*>(base);
+      base += L.rc_bytes;
+      m.rc_scale = reinterpret_cast<float*>(base);
+      base += L.rcs_bytes;
       m.stats = stats ? stats + sel[k].stats_index * MUON_STATS_PER_MATRIX : nullptr;
       m.decay = float(1.0 - lr * wd);
       // Shape factor: Moonlight 0.2*sqrt(max(rows, cols)), or Keller
@@ -427,8 +439,11 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       }
     }
     if (reduce) {
-      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, s), 5, s, t0))) return st;
+      const bool rc = h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON;
+      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, rc, s), 5, s, t0))) return st;
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, s), 6, s, t0))) return st;
+      if (rc && ((t0 = prof_start(s)), (st = finish_launch(launch_rc_finalize(bt, w_one, h.variant, s), 6, s, t0))))
+        return st;
     }
     if (w_tail.begin[nsel] > 0 &&  // every group may have been finished by its last update
         ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),

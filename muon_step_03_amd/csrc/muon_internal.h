@@ -14,6 +14,8 @@
 //   head    [count][head_tiles]     per-tile partial sums of u^2
 //   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
 //   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
+//   rc      [count][tail_tiles][128] per-tile row and column sums of O^2
+//   rcs     [count][rows + cols]    row and column scales of O (NorMuon, MeqMuon)
 // Element type of X, A, B is bf16 (bit pattern in uint16_t) on the bf16 path
 // and float on the fp32 path.
 #pragma once
@@ -90,6 +92,8 @@ struct MatGroup {
   int64_t a_stride;    // elements between matrices in A/B
   float* head_part;
   float* tail_part;
+  float* rc_part;      // [count][tail_tiles][128]: per-tile row and column sums of O^2
+  float* rc_scale;     // [count][rows + cols]: row, then column scales of O
   float* scal;
   float* stats;        // MUON_STATS_PER_MATRIX per matrix, or null
   float decay;         // 1 - lr*wd
@@ -223,9 +227,13 @@ struct AdamBatch {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_head(const Batch& bt, const Work& wk, bool bf16, float momentum, hipStream_t s);
 hipError_t launch_norm_finalize(const Batch& bt, const Work& wk, hipStream_t s);
-hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps,
+// `rc`: also the per-tile row and column sums of O^2 (NorMuon, MeqMuon).
+hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps, bool rc,
                               hipStream_t s);
 hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
+// NorMuon / MeqMuon: row and column norms of O, the direction to equalise and
+// the per-row and per-column scales (one block per matrix).
+hipError_t launch_rc_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
 // `reduced`: tail_finalize ran, so the per-matrix coefficient and MuonH
 // scale are read from the scalars (otherwise 0 and 1).
 hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,

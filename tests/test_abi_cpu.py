@@ -50,7 +50,8 @@ def test_status_strings(L):
 
 def ws_formula(count, rows, cols, dtype):
     """Workspace size from the layout the library documents (X0, X1, A, B,
-    head/tail partials, per-matrix scalars; 256-byte aligned regions)."""
+    head/tail partials, per-matrix scalars, row/column partials and scales;
+    256-byte aligned regions)."""
     tile_p, tile_q = (128, 256) if dtype == _lib.MUON_DTYPE_BF16 else (64, 64)
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     p, q = min(rows, cols), max(rows, cols)
@@ -59,7 +60,8 @@ def ws_formula(count, rows, cols, dtype):
     head = (pp // 64) * (qp // 64)
     tail = math.ceil(rows / 64) * math.ceil(cols / 64)
     return (2 * al(count * pp * qp * es) + 2 * al(count * pp * pp * es) + al(count * head * 4)
-            + al(count * tail * 12) + al(count * 8 * 4) + 256)
+            + al(count * tail * 12) + al(count * 8 * 4) + al(count * tail * 128 * 4)
+            + al(count * (rows + cols) * 4) + 256)
 
 
 @pytest.mark.parametrize("shape", [(256, 512), (768, 3072), (3072, 768), (100, 300), (1, 1),
@@ -108,8 +110,8 @@ def call_step(L, W=W, G=G, M=M, rows=64, cols=128, dtype=0, ws=WS, wsb=1 << 30, 
     (dict(ns=-1), 1), (dict(ns=_lib.MUON_MAX_NS_STEPS + 1), 1),
     (dict(lr=float("nan")), 1), (dict(mom=float("inf")), 1), (dict(wd=float("-inf")), 1),
     (dict(a=float("nan")), 1), (dict(b=float("inf")), 1), (dict(c=float("nan")), 1),
-    (dict(variant=3), 1), (dict(variant=-1), 1), (dict(variant=0x200), 1),
-    (dict(variant=0x103), 1),
+    (dict(variant=5), 1), (dict(variant=-1), 1), (dict(variant=0x200), 1),
+    (dict(variant=0x105), 1),
     (dict(ws=None), 1), (dict(wsb=1000), 4),
     (dict(G=W), 1),                          # W and G alias
     (dict(M=W + 64), 1),                     # M overlaps W
@@ -119,7 +121,7 @@ def test_step_validation(L, kw, status):
     assert call_step(L, **kw) == status
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 0x100, 0x101, 0x102])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 0x100, 0x101, 0x102, 0x103, 0x104])
 def test_valid_variants_pass_validation(L, variant):
     """Valid variants get past argument checks (to the workspace check here)."""
     assert call_step(L, variant=variant, wsb=16) == _lib.MUON_ERR_WORKSPACE_TOO_SMALL

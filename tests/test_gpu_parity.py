@@ -405,3 +405,79 @@ def test_errors_surface_as_exceptions():
         muon_step(W, G, M, ns_steps=-1)
     with pytest.raises(ValueError):
         muon_step(W[0], G[0], M[0])
+
+
+# ------------------------------------------------------ NorMuon and MeqMuon
+def spreads(O):
+    """std/mean of the row norms and of the column norms of O (fp64)."""
+    rn, cn = np.linalg.norm(O, axis=1), np.linalg.norm(O, axis=0)
+    return float(np.std(rn) / np.mean(rn)), float(np.std(cn) / np.mean(cn))
+
+
+def recovered_o(W0, W1, shape, wd=0.1, lr=0.02):
+    step = lr * 0.2 * math.sqrt(max(shape))
+    return -(f64(W1) - (1 - lr * wd) * f64(W0)) / step
+
+
+NORM_SHAPES = [(96, 256), (256, 96), (200, 200), (130, 70), (70, 130)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", NORM_SHAPES)
+@pytest.mark.parametrize("heavy", ["row", "col"])
+@pytest.mark.parametrize("variant", ["normuon", "meqmuon"])
+def test_row_column_equalisation(dtype, shape, heavy, variant):
+    """Against the oracle, with a dominant gradient row or column so that
+    both MeqMuon directions occur; the direction is a floating-point choice,
+    so the inputs keep the two spreads apart by a margin that fp32 and fp64
+    cannot disagree on.  On the GPU's own output, the equalised direction's
+    norms are equal."""
+    W, G, M = inputs(*shape, dtype, seed=hash((shape, heavy)) % 10000, m_std=1e-3)
+    if heavy == "row":
+        G[shape[0] // 3] *= 20
+    else:
+        G[:, shape[1] // 3] *= 20
+    _, _, st_ref = oracle_step(W, G, M, variant="muon")
+    Wm, _, _ = oracle_step(W, G, M, variant="muon")
+    O = recovered_o(W, torch.from_numpy(Wm), shape)
+    sr, sc = spreads(O)
+    assert abs(sr - sc) > 1e-2 * max(sr, sc), (sr, sc)
+    rows = variant == "normuon" or sr >= sc
+    W1, M1, st = gpu_step(W, G, M, variant=variant)
+    check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st)
+    On = recovered_o(W, W1, shape)
+    n = np.linalg.norm(On, axis=1 if rows else 0)
+    tol = 1e-4 if dtype == torch.float32 else 3e-2
+    assert np.max(np.abs(n / np.mean(n) - 1)) < tol
+
+
+@pytest.mark.parametrize("variant", ["normuon", "meqmuon"])
+def test_equalisation_gpt160m_grouped(variant):
+    """The grouped launch over the 72 GPT-160M matrices (three shape groups).
+    A nearly orthogonal square O has row and column spreads of about 1 % and
+    close to each other, so MeqMuon's choice can go either way between fp32
+    and fp64: the direction the GPU took is read off its output (the
+    equalised side), must be the oracle's wherever the two spreads differ by
+    more than 2 %, and the result is compared with the oracle's step for
+    that direction."""
+    w = wl.WORKLOADS["gpt160m"]
+    Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
+    W0, Gs, M0 = run_workload(w, 0, Ws, Ms, variant)
+    for gi, i in sampled(w):
+        shape = (w.groups[gi].rows, w.groups[gi].cols)
+        Wm, Mr, _ = oracle_step(W0[gi][i], Gs[gi][i], M0[gi][i], variant="muon")
+        O = recovered_o(W0[gi][i], torch.from_numpy(Wm), shape)
+        On = recovered_o(W0[gi][i], Ws[gi][i], shape)
+        rn, cn = np.linalg.norm(On, axis=1), np.linalg.norm(On, axis=0)
+        gpu_rows = np.std(rn) / np.mean(rn) <= np.std(cn) / np.mean(cn)
+        sr, sc = spreads(O)
+        if variant == "normuon" or abs(sr - sc) > 2e-2 * max(sr, sc):
+            assert gpu_rows == (variant == "normuon" or sr >= sc), (sr, sc)
+        ref = oracle.normuon_rows(O) if gpu_rows else oracle.normuon_cols(O)
+        step = 0.02 * 0.2 * math.sqrt(max(shape))
+        Wr = (1 - 0.002) * f64(W0[gi][i]) - step * ref
+        e = relF(f64(Ws[gi][i]) - f64(W0[gi][i]), Wr - f64(W0[gi][i]))
+        assert e <= TOL_BF16, e
+        assert relF(f64(Ms[gi][i]), Mr) <= TOL_M
+        print(f"gpt160m {w.groups[gi]} #{i} {variant}: spreads {sr:.4f}/{sc:.4f}, "
+              f"{'rows' if gpu_rows else 'cols'}, relF(dW) = {e:.2e}")

@@ -322,12 +322,16 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
         bfr[ni] = lds_frag_rows(sB, wn * 32 * WN + ni * 32 + (lane & 31), ch);
     }
   };
+  // The B fragment goes in the MFMA's first operand slot: the accumulator
+  // then holds the tile transposed, so that lane l, register 4g + jj is row
+  // l%32, column 8g + 4(l/32) + jj of its 32x32 block: 4 consecutive columns
+  // of one row per 4 registers (16-byte LDS writes in the epilogue).
   auto mfmas = [&](const bf16x8_t (&af)[WM], const bf16x8_t (&bfr)[WN]) {
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < WN; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
   };
   // Waits until the loads of `stage` are done, given that the last stage
   // issued so far is `issued` (capped at nk-1): exactly the loads of the
@@ -400,7 +404,9 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
     for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= (MODE == MODE_POLY ? c2 : alpha);
-  constexpr int TP = BN + 8;                 // fp32 staging row pitch (floats)
+  // fp32 staging row pitch (floats): 4 mod 64 banks, so the 16-byte writes of
+  // 16 lanes (16 consecutive rows, one column) cover all banks once.
+  constexpr int TP = BN + 4;
   static_assert(64 * TP * 4 <= S * STAGE_BYTES, "staging");
   LDS_AS float* T = (LDS_AS float*)smem;
   constexpr int CPR = BN / 8;                // 8-element chunks per row
@@ -415,15 +421,15 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
     for (int mi = 0; mi < WM; ++mi) {
       const int blk = wm * WM + mi;
       if ((blk >> 1) != pass) continue;
-      // MFMA 32x32 output layout: lane l, register r holds row
-      // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block.
+      const int row = (blk & 1) * 32 + (lane & 31);
 #pragma unroll
       for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (blk & 1) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int col = wn * 32 * WN + ni * 32 + (lane & 31);
-          T[row * TP + col] = acc[mi][ni][r];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = wn * 32 * WN + ni * 32 + 8 * g4 + 4 * (lane >> 5);
+          *(LDS_AS f32x4_t*)(T + row * TP + col) =
+              f32x4_t{acc[mi][ni][4 * g4], acc[mi][ni][4 * g4 + 1], acc[mi][ni][4 * g4 + 2],
+                      acc[mi][ni][4 * g4 + 3]};
         }
     }
   };
@@ -449,8 +455,9 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
       v[2 * e + 1] = fmaf(lin_coef, __uint_as_float(w[e] & 0xffff0000u), v[2 * e + 1]);
     }
   };
-  auto finish = [&](int pass) {
-    uint4 lin[kLin ? CHUNKS : 1], lin_m[kLin ? MCH : 1];
+  // Loads of the linear term for one pass, issued before the pass's LDS
+  // staging and barriers so that their latency overlaps them.
+  auto load_lin = [&](int pass, uint4 (&lin)[kLin ? CHUNKS : 1], uint4 (&lin_m)[kLin ? MCH : 1]) {
     if (kLin) {
 #pragma unroll
       for (int u = 0; u < CHUNKS; ++u) {
@@ -467,6 +474,9 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
         }
       }
     }
+  };
+  auto finish = [&](int pass, const uint4 (&lin)[kLin ? CHUNKS : 1],
+                    const uint4 (&lin_m)[kLin ? MCH : 1]) {
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int q = t + NT * u;
@@ -577,13 +587,20 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
 
 #pragma unroll
   for (int pass = 0; pass < BM / 64; ++pass) {
+    // The polynomial has registers to spare for loading its b*A rows before
+    // the staging; the update (accumulators of a 128x256 tile) loads them
+    // after it.
+    uint4 lin[kLin ? CHUNKS : 1], lin_m[kLin ? MCH : 1];
+    if (MODE == MODE_POLY) load_lin(pass, lin, lin_m);
     block_barrier();  // stage buffers (pass 0) / the previous pass's T no longer read
     stage(pass);
     block_barrier();
-    if (fuse)
+    if (fuse) {
       finish_tail(pass);
-    else
-      finish(pass);
+    } else {
+      if (MODE != MODE_POLY) load_lin(pass, lin, lin_m);
+      finish(pass, lin, lin_m);
+    }
   }
   }  // tiles of group oi
   base += cnt;

@@ -195,6 +195,52 @@ def stacked_group(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor) -> _lib.Muo
     return _lib.MuonGroup(n, r, c, None, None, None, W.data_ptr(), G.data_ptr(), M.data_ptr())
 
 
+def chunk_size(shapes, dtype: torch.dtype, max_workspace_bytes: int) -> int:
+    """Matrices per shape per grouped call: the fewest calls such that one
+    call over min(c, count) matrices of every (count, rows, cols) shape needs
+    at most ``max_workspace_bytes`` of workspace (which grows with c), with
+    the matrices spread evenly over those calls."""
+    shapes = [(int(n), int(r), int(k)) for n, r, k in shapes]
+    if not shapes or min(n for n, _, _ in shapes) < 1:
+        raise ValueError("chunk_size needs non-empty shape groups")
+
+    def need(c):
+        return workspace_bytes_grouped([_lib.MuonGroup(min(c, n), r, k, None, None, None,
+                                                       None, None, None)
+                                        for n, r, k in shapes], dtype)
+
+    lo, hi = 1, max(n for n, _, _ in shapes)
+    if need(lo) > max_workspace_bytes:
+        raise ValueError(f"one matrix of each shape needs {need(lo)} workspace bytes, "
+                         f"more than {max_workspace_bytes}")
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if need(mid) <= max_workspace_bytes:
+            lo = mid
+        else:
+            hi = mid - 1
+    calls = -(-max(n for n, _, _ in shapes) // lo)
+    return -(-max(n for n, _, _ in shapes) // calls)   # same number of calls, even chunks
+
+
+def stacked_chunks(stacks, dtype: torch.dtype, max_workspace_bytes: int):
+    """Split a model given as (W, G, M) [count, rows, cols] stacks into
+    successive grouped calls whose workspace fits ``max_workspace_bytes``.
+
+    Call k takes matrices [k c, (k+1) c) of every stack, c = :func:`chunk_size`;
+    a model that fits whole is one call.  Returns the list of calls (each a
+    list of groups for :func:`muon_step_grouped`) and the workspace bytes the
+    largest call needs.  Every matrix's step is independent of the others, so
+    running the calls in order on one stream is the whole step."""
+    stacks = list(stacks)
+    c = chunk_size([tuple(W.shape) for W, _, _ in stacks], dtype, max_workspace_bytes)
+    counts = [int(W.shape[0]) for W, _, _ in stacks]
+    calls = [[stacked_group(W[k:k + c], G[k:k + c], M[k:k + c])
+              for (W, G, M), n in zip(stacks, counts) if k < n]
+             for k in range(0, max(counts), c)]
+    return calls, max(workspace_bytes_grouped(call, dtype) for call in calls)
+
+
 def table_group(count, rows, cols, W_table, G_table, M_table) -> _lib.MuonGroup:
     """A group over device pointer tables (int64 GPU tensors of data pointers)."""
     return _lib.MuonGroup(count, rows, cols, W_table.data_ptr(), G_table.data_ptr(),

@@ -47,7 +47,11 @@ constexpr int kEwTile = 64;        // head/tail tile edge (elements)
 #endif
 constexpr int kUpdWaves = MUON_UPD_WAVES;
 constexpr int kUpdBlocksPerCU = kUpdWaves == 8 ? 1 : 2;
-constexpr int kSyrkBlocksPerCU = 2;
+// Blocks per CU of the symmetric products (2: four stages of 16 KB each).
+#ifndef MUON_SYRK_OCC
+#define MUON_SYRK_OCC 2
+#endif
+constexpr int kSyrkBlocksPerCU = MUON_SYRK_OCC;
 constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
 constexpr int kUpdTileM = MUON_UPD_TILE_M;  // update: rows (along p)
 constexpr int kUpdTileN = MUON_UPD_TILE_N;  // update: columns (along q)

@@ -260,3 +260,43 @@ def test_aux_workload_matches_page_hyperparameters():
     from muon_step_03_amd import api
     assert api.AUX_BETAS == oracle.AUX_BETAS and api.AUX_EPS == oracle.AUX_EPS
     assert api.AUX_WEIGHT_DECAY == oracle.AUX_WEIGHT_DECAY and api.AUX_LR == oracle.AUX_LR
+
+
+# ------------------------------------------ chunking a model under a budget
+def _need(shapes, c):
+    import torch
+    from muon_step_03_amd import workspace_bytes_grouped
+    return workspace_bytes_grouped([_lib.MuonGroup(min(c, n), r, k, None, None, None, None,
+                                                   None, None) for n, r, k in shapes],
+                                   torch.bfloat16)
+
+
+@pytest.mark.parametrize("budget_gib", [0.5, 4, 16, 32, 48, 200])
+def test_chunk_size_fewest_even_calls(budget_gib):
+    """The chunk fits the budget, no smaller number of calls would, and the
+    chunks are as even as that number of calls allows."""
+    import torch
+    from muon_step_03_amd import chunk_size
+    shapes = [(1024, 2048, 5632), (1024, 5632, 2048)]
+    budget = int(budget_gib * 2**30)
+    c = chunk_size(shapes, torch.bfloat16, budget)
+    calls = math.ceil(1024 / c)
+    assert _need(shapes, c) <= budget
+    assert c == math.ceil(1024 / calls)
+    if calls > 1:
+        assert _need(shapes, math.ceil(1024 / (calls - 1))) > budget
+    else:
+        assert c == 1024
+
+
+def test_chunk_size_whole_model_and_errors():
+    import torch
+    from muon_step_03_amd import chunk_size
+    shapes = [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)]
+    assert chunk_size(shapes, torch.bfloat16, 1 << 40) == 48
+    assert chunk_size(shapes, torch.bfloat16, _need(shapes, 48)) == 48
+    assert chunk_size(shapes, torch.bfloat16, _need(shapes, 48) - 1) == 24
+    with pytest.raises(ValueError):
+        chunk_size(shapes, torch.bfloat16, _need(shapes, 1) - 1)
+    with pytest.raises(ValueError):
+        chunk_size([], torch.bfloat16, 1 << 30)

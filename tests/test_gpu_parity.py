@@ -380,6 +380,38 @@ def test_stress_matrices_sampled():
         print(f"stress {small.groups[gi]} #{i}: relF(dW) = {e:.2e}")
 
 
+@pytest.mark.timeout(900)
+def test_stress_full_size_chunked():
+    """The whole 2k-hidden stress set (1024 matrices of 2048x5632 and 1024 of
+    5632x2048, heavy-tailed gradient rows: 23.6 G elements, 189 GB of W, G
+    and M) in the calls the benchmark times: its workspace would not fit
+    beside the tensors, so the step runs as a few grouped calls over even
+    chunks of both groups.  The first and last matrix of each shape, copied
+    before the step, are checked against the oracle."""
+    from muon_step_03_amd import stacked_chunks
+    w = wl.WORKLOADS["stress2k"]
+    torch.cuda.empty_cache()
+    Ws, Gs, Ms = wl.make_weights(w, DEV), wl.make_grads(w, 0, DEV), wl.make_momentum(w, DEV)
+    torch.cuda.empty_cache()
+    picks = sampled(w)
+    before = {(gi, i): (Ws[gi][i].clone(), Gs[gi][i].clone(), Ms[gi][i].clone()) for gi, i in picks}
+    calls, ws_bytes = stacked_chunks(zip(Ws, Gs, Ms), torch.bfloat16, 32 << 30)
+    assert len(calls) > 1
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    for groups in calls:
+        muon_step_grouped(groups, torch.bfloat16, workspace=ws, **HP)
+    torch.cuda.synchronize()
+    print(f"stress2k: {len(calls)} calls of {calls[0][0].count} matrices per shape, "
+          f"workspace {ws_bytes / 2**30:.1f} GiB", flush=True)
+    after = {k: (Ws[k[0]][k[1]].cpu(), Ms[k[0]][k[1]].cpu()) for k in picks}
+    del Ws, Gs, Ms, ws, calls
+    torch.cuda.empty_cache()
+    for gi, i in picks:
+        W0, G, M0 = (x.cpu() for x in before[(gi, i)])
+        e, _, _ = check_against_oracle(W0, G, M0, *after[(gi, i)])
+        print(f"stress2k {w.groups[gi]} #{i}: relF(dW) = {e:.2e}", flush=True)
+
+
 def test_optimizer_front_end_two_steps():
     shapes = [(256, 256), (256, 1024), (1024, 256), (256, 256)]
     params = [torch.nn.Parameter(wl.random_matrix(*s, 0.02, 500 + i, torch.bfloat16, DEV))

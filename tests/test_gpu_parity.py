@@ -460,27 +460,42 @@ NORM_SHAPES = [(96, 256), (256, 96), (200, 200), (130, 70), (70, 130)]
 @pytest.mark.parametrize("variant", ["normuon", "meqmuon"])
 def test_row_column_equalisation(dtype, shape, heavy, variant):
     """Against the oracle, with a dominant gradient row or column so that
-    both MeqMuon directions occur; the direction is a floating-point choice,
-    so the inputs keep the two spreads apart by a margin that fp32 and fp64
-    cannot disagree on.  On the GPU's own output, the equalised direction's
-    norms are equal."""
-    W, G, M = inputs(*shape, dtype, seed=hash((shape, heavy)) % 10000, m_std=1e-3)
+    both MeqMuon directions occur.  The direction is a floating-point choice
+    on spreads of a few percent, which the bf16 Newton-Schulz iteration moves
+    by a few percent of themselves: the inputs (drawn on the host, fixed
+    seeds) keep the two spreads at least 16 % apart, and the test asserts a
+    10 % margin.  On the GPU's own output, the equalised direction's norms
+    are equal and the other direction's are not."""
+    seed = 7100 + 10 * NORM_SHAPES.index(shape) + (heavy == "col")
+    W = wl.random_matrix(*shape, 0.02, seed, dtype)
+    G = wl.random_matrix(*shape, 1e-3, seed + 1, torch.float32)
     if heavy == "row":
         G[shape[0] // 3] *= 20
     else:
         G[:, shape[1] // 3] *= 20
-    _, _, st_ref = oracle_step(W, G, M, variant="muon")
+    G = G.to(dtype)
+    M = wl.random_matrix(*shape, 1e-3, seed + 2, torch.float32)
     Wm, _, _ = oracle_step(W, G, M, variant="muon")
     O = recovered_o(W, torch.from_numpy(Wm), shape)
     sr, sc = spreads(O)
-    assert abs(sr - sc) > 1e-2 * max(sr, sc), (sr, sc)
+    assert abs(sr - sc) > 0.1 * max(sr, sc), (sr, sc)
     rows = variant == "normuon" or sr >= sc
+    W, G, M = W.to(DEV), G.to(DEV), M.to(DEV)
     W1, M1, st = gpu_step(W, G, M, variant=variant)
     check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st)
     On = recovered_o(W, W1, shape)
     n = np.linalg.norm(On, axis=1 if rows else 0)
-    tol = 1e-4 if dtype == torch.float32 else 3e-2
-    assert np.max(np.abs(n / np.mean(n) - 1)) < tol
+    other = np.linalg.norm(On, axis=0 if rows else 1)
+    # bf16: rounding W' to bf16 alone leaves the equalised norms 1.5e-3 to
+    # 3.5e-3 apart on these inputs; the other direction's norms stay at
+    # least 5 % apart
+    tol = 1e-4 if dtype == torch.float32 else 1e-2
+    dev = np.max(np.abs(n / np.mean(n) - 1))
+    dev_other = np.max(np.abs(other / np.mean(other) - 1))
+    print(f"{variant} {shape} heavy {heavy} {dtype}: spreads rows {sr:.4f} cols {sc:.4f}, "
+          f"equalised {'rows' if rows else 'cols'} to {dev:.1e} (other {dev_other:.1e})")
+    assert dev < tol
+    assert dev_other > 3e-2
 
 
 @pytest.mark.parametrize("variant", ["normuon", "meqmuon"])

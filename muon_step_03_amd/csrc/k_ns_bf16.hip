@@ -91,6 +91,24 @@ struct Cfg<MODE_GRAM> {
 };
 template <>
 struct Cfg<MODE_POLY> : Cfg<MODE_GRAM> {};
+// Symmetric products of large matrices: 256x256 tiles, 8 waves of 128x64,
+// one block per CU (four stages of 32 KiB).  Every operand byte brought into
+// a CU feeds twice the MFMA work of a 128x128 tile, which halves the L2 and
+// fabric traffic of the long-K Gram products of wide matrices.
+struct CfgSyrkBig {
+  static constexpr int BM = kSyrkBigTile, BN = kSyrkBigTile, NW = 8, WGM = 2, WGN = 4;
+  static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int STAGES = 4;
+  static constexpr int OCC = 1;
+};
+// Update of large matrices: 256x256 tiles, 8 waves of 128x64, one block
+// per CU (four stages of 32 KiB).
+struct CfgUpdBig {
+  static constexpr int BM = kUpdBigTile, BN = kUpdBigTile, NW = 8, WGM = 2, WGN = 4;
+  static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int STAGES = 4;
+  static constexpr int OCC = 1;
+};
 template <>
 struct Cfg<MODE_UPDATE> {
   static constexpr int BM = kUpdTileM, BN = kUpdTileN, NW = kUpdWaves, WGM = MUON_UPD_WGM,
@@ -164,10 +182,9 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_kernel(
+template <int MODE, class C>
+__global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     Batch bt, TileList tl, int iter, float c1, float c2) {
-  using C = Cfg<MODE>;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES;
   constexpr int NT = 64 * C::NW;                     // threads per block
   constexpr int A_BYTES = BM * BK * 2;
@@ -587,18 +604,19 @@ __global__ __launch_bounds__(64 * Cfg<MODE>::NW, Cfg<MODE>::OCC) void ns_bf16_ke
 
 #pragma unroll
   for (int pass = 0; pass < BM / 64; ++pass) {
-    // The polynomial has registers to spare for loading its b*A rows before
-    // the staging; the update (accumulators of a 128x256 tile) loads them
-    // after it.
+    // The polynomial of 64x64 wave tiles has registers to spare for loading
+    // its b*A rows before the staging; larger wave tiles (the update's, the
+    // 256x256 symmetric tiles') load them after it.
     uint4 lin[kLin ? CHUNKS : 1], lin_m[kLin ? MCH : 1];
-    if (MODE == MODE_POLY) load_lin(pass, lin, lin_m);
+    constexpr bool kEarlyLin = MODE == MODE_POLY && WM * WN <= 4;
+    if (kEarlyLin) load_lin(pass, lin, lin_m);
     block_barrier();  // stage buffers (pass 0) / the previous pass's T no longer read
     stage(pass);
     block_barrier();
     if (fuse) {
       finish_tail(pass);
     } else {
-      if (MODE != MODE_POLY) load_lin(pass, lin, lin_m);
+      if (!kEarlyLin) load_lin(pass, lin, lin_m);
       finish(pass, lin, lin_m);
     }
   }
@@ -611,16 +629,32 @@ inline dim3 grid_of(const TileList& tl) { return dim3(unsigned(8 * tl.blocks_per
 
 }  // namespace
 
-hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, hipStream_t s) {
-  hipLaunchKernelGGL(ns_bf16_kernel<MODE_GRAM>, grid_of(tl), dim3(64 * Cfg<MODE_GRAM>::NW), 0, s, bt, tl, iter, 0.f, 0.f);
+hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_GRAM, CfgSyrkBig>), grid_of(tl), dim3(64 * CfgSyrkBig::NW),
+                       0, s, bt, tl, iter, 0.f, 0.f);
+  else
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_GRAM, Cfg<MODE_GRAM>>), grid_of(tl),
+                       dim3(64 * Cfg<MODE_GRAM>::NW), 0, s, bt, tl, iter, 0.f, 0.f);
   return hipGetLastError();
 }
-hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, hipStream_t s) {
-  hipLaunchKernelGGL(ns_bf16_kernel<MODE_POLY>, grid_of(tl), dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, b, c);
+hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, bool big, hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_POLY, CfgSyrkBig>), grid_of(tl), dim3(64 * CfgSyrkBig::NW),
+                       0, s, bt, tl, 0, b, c);
+  else
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_POLY, Cfg<MODE_POLY>>), grid_of(tl),
+                       dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, b, c);
   return hipGetLastError();
 }
-hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, hipStream_t s) {
-  hipLaunchKernelGGL(ns_bf16_kernel<MODE_UPDATE>, grid_of(tl), dim3(64 * Cfg<MODE_UPDATE>::NW), 0, s, bt, tl, iter, a, 0.f);
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, bool big,
+                              hipStream_t s) {
+  if (big)
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, CfgUpdBig>), grid_of(tl), dim3(64 * CfgUpdBig::NW),
+                       0, s, bt, tl, iter, a, 0.f);
+  else
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, Cfg<MODE_UPDATE>>), grid_of(tl),
+                       dim3(64 * Cfg<MODE_UPDATE>::NW), 0, s, bt, tl, iter, a, 0.f);
   return hipGetLastError();
 }
 

@@ -138,13 +138,25 @@ int check_group(const muon_group& g, int dtype) {
 struct PhaseTiles {
   int64_t head, gram, update, tail;
 };
+// bf16 matrices whose symmetric products take the 256x256 tiles.
+bool syrk_big(const Layout& L, bool bf16) {
+  return bf16 && L.p >= kSyrkBigMinP && L.p_pad % kSyrkBigTile == 0;
+}
+bool upd_big(const Layout& L, bool bf16) {
+  return syrk_big(L, bf16) && L.q_pad % kUpdBigTile == 0;
+}
 PhaseTiles phase_tiles(const Layout& L, bool bf16) {
   PhaseTiles t;
-  const int64_t ts = bf16 ? kSyrkTile : kF32Tile;
+  const int64_t ts = bf16 ? (syrk_big(L, bf16) ? kSyrkBigTile : kSyrkTile) : kF32Tile;
   const int64_t nt = L.p_pad / ts;
   t.head = L.head_tiles;
   t.gram = nt * (nt + 1) / 2;
-  t.update = bf16 ? (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN) : nt * (L.q_pad / kF32Tile);
+  if (!bf16)
+    t.update = (L.p_pad / kF32Tile) * (L.q_pad / kF32Tile);
+  else if (upd_big(L, bf16))
+    t.update = (L.p_pad / kUpdBigTile) * (L.q_pad / kUpdBigTile);
+  else
+    t.update = (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN);
   t.tail = L.tail_tiles;
   return t;
 }
@@ -226,18 +238,21 @@ int cus_per_xcd() {
   return n / 8;
 }
 
-// Static tile list of one persistent Newton-Schulz launch: groups with more
-// K steps per tile first (they finish last otherwise), up to the given
-// number of resident blocks per XCD.
+// Static tile list of one persistent Newton-Schulz launch over the groups
+// with tiles in it (tiles_per_matrix > 0): groups with more K steps per tile
+// first (they finish last otherwise), up to the given number of resident
+// blocks per XCD.  An empty list (ngroups 0) is not launched.
 TileList make_tile_list(const Batch& bt, const int64_t* tiles_per_matrix, const int64_t* k_len,
                         int blocks_per_xcd_max) {
   TileList tl{};
-  tl.ngroups = bt.ngroups;
   int order[kMaxGroups];
-  for (int k = 0; k < bt.ngroups; ++k) order[k] = k;
-  std::stable_sort(order, order + bt.ngroups, [&](int a, int b) { return k_len[a] > k_len[b]; });
+  int n = 0;
+  for (int k = 0; k < bt.ngroups; ++k)
+    if (tiles_per_matrix[k] > 0) order[n++] = k;
+  std::stable_sort(order, order + n, [&](int a, int b) { return k_len[a] > k_len[b]; });
+  tl.ngroups = n;
   int64_t per_xcd = 0;
-  for (int i = 0; i < bt.ngroups; ++i) {
+  for (int i = 0; i < n; ++i) {
     const int k = order[i];
     tl.group[i] = k;
     tl.tiles[i] = int(tiles_per_matrix[k]);
@@ -397,23 +412,32 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     }
     bool any_fused = false;
     for (int k = 0; k < nsel; ++k) any_fused = any_fused || bt.g[k].fuse;
-    TileList tl_gram{}, tl_poly{}, tl_upd{};
+    // Symmetric products: one launch over the groups in 128x128 tiles and
+    // one over the large groups in 256x256 tiles (each only if non-empty).
+    TileList tl_gram{}, tl_poly{}, tl_gram_big{}, tl_poly_big{}, tl_upd{}, tl_upd_big{};
     if (bf16) {
       const int cpx = cus_per_xcd();
       if (cpx == 0) {
         g_last_hip_error = int(hipErrorInvalidDevice);
         return MUON_ERR_HIP;
       }
-      int64_t nt[kMaxGroups], nu[kMaxGroups], kq[kMaxGroups], kp[kMaxGroups];
+      int64_t nt[kMaxGroups], ntb[kMaxGroups], nu[kMaxGroups], nub[kMaxGroups], kq[kMaxGroups],
+          kp[kMaxGroups];
       for (int k = 0; k < nsel; ++k) {
-        nt[k] = w_gram.tiles[k];
-        nu[k] = w_upd.tiles[k];
+        const bool big = syrk_big(sel[k].L, true), ubig = upd_big(sel[k].L, true);
+        nt[k] = big ? 0 : w_gram.tiles[k];
+        ntb[k] = big ? w_gram.tiles[k] : 0;
+        nu[k] = ubig ? 0 : w_upd.tiles[k];
+        nub[k] = ubig ? w_upd.tiles[k] : 0;
         kq[k] = bt.g[k].q_pad;
         kp[k] = bt.g[k].p_pad;
       }
       tl_gram = make_tile_list(bt, nt, kq, kSyrkBlocksPerCU * cpx);
       tl_poly = make_tile_list(bt, nt, kp, kSyrkBlocksPerCU * cpx);
+      tl_gram_big = make_tile_list(bt, ntb, kq, kSyrkBigBlocksPerCU * cpx);
+      tl_poly_big = make_tile_list(bt, ntb, kp, kSyrkBigBlocksPerCU * cpx);
       tl_upd = make_tile_list(bt, nu, kp, kUpdBlocksPerCU * cpx);
+      tl_upd_big = make_tile_list(bt, nub, kp, kUpdBigBlocksPerCU * cpx);
     }
     hipEvent_t t0 = nullptr;
     Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};
@@ -426,12 +450,28 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     if ((t0 = prof_start(s)), (st = finish_launch(launch_norm_finalize(bt, w_one, s), 1, s, t0))) return st;
     for (int it = 0; it < ns_steps; ++it) {
       if (bf16) {
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram, it, s), 2, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.b, h.c, s), 3, s, t0))) return st;
-        TileList tl = tl_upd;
-        tl.fuse_tail = (it == ns_steps - 1 && any_fused) ? 1 : 0;
-        const int ph = tl.fuse_tail ? kPhaseUpdateTail : 4;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, h.a, s), ph, s, t0))) return st;
+        if (tl_gram.ngroups &&
+            ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram, it, false, s), 2, s, t0))))
+          return st;
+        if (tl_gram_big.ngroups &&
+            ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram_big, it, true, s), 2, s, t0))))
+          return st;
+        if (tl_poly.ngroups &&
+            ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.b, h.c, false, s), 3, s, t0))))
+          return st;
+        if (tl_poly_big.ngroups &&
+            ((t0 = prof_start(s)),
+             (st = finish_launch(launch_poly_bf16(bt, tl_poly_big, h.b, h.c, true, s), 3, s, t0))))
+          return st;
+        const int fuse_tail = (it == ns_steps - 1 && any_fused) ? 1 : 0;
+        const int ph = fuse_tail ? kPhaseUpdateTail : 4;
+        for (int big = 0; big < 2; ++big) {
+          TileList tl = big ? tl_upd_big : tl_upd;
+          if (!tl.ngroups) continue;
+          tl.fuse_tail = fuse_tail;
+          if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, h.a, big != 0, s), ph, s, t0)))
+            return st;
+        }
       } else {
         if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_f32(bt, w_gram, it, s), 2, s, t0))) return st;
         if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_f32(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;

@@ -53,6 +53,17 @@ constexpr int kUpdBlocksPerCU = kUpdWaves == 8 ? 1 : 2;
 #endif
 constexpr int kSyrkBlocksPerCU = MUON_SYRK_OCC;
 constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
+// Large matrices (short side at least kSyrkBigMinP, padded short side a
+// multiple of kSyrkBigTile) take the symmetric products in 256x256 tiles.
+#ifndef MUON_SYRK_BIG_MIN_P
+#define MUON_SYRK_BIG_MIN_P 1024
+#endif
+constexpr int kSyrkBigTile = 256;
+constexpr int kSyrkBigMinP = MUON_SYRK_BIG_MIN_P;
+constexpr int kSyrkBigBlocksPerCU = 1;
+// ... and their update in 256x256 tiles (one block per CU).
+constexpr int kUpdBigTile = 256;
+constexpr int kUpdBigBlocksPerCU = 1;
 constexpr int kUpdTileM = MUON_UPD_TILE_M;  // update: rows (along p)
 constexpr int kUpdTileN = MUON_UPD_TILE_N;  // update: columns (along q)
 constexpr int kBf16PadP = kSyrkTile > kUpdTileM ? kSyrkTile : kUpdTileM;
@@ -244,9 +255,11 @@ hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const H
                              bool reduced, hipStream_t s);
 // Newton-Schulz products.  `iter` selects X0/X1 and the first-iteration norm
 // scaling.
-hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, hipStream_t s);
-hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, hipStream_t s);
-hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, hipStream_t s);
+hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s);
+hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, bool big,
+                            hipStream_t s);
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, bool big,
+                              hipStream_t s);
 hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s);
 hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
 hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);

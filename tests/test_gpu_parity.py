@@ -81,6 +81,21 @@ def test_bf16_ragged(shape, variant):
     print(f"bf16 {shape} {variant}: relF(dW) = {e:.2e}")
 
 
+# Short side of at least 1024 with a padded short side that is a multiple of
+# 256: the symmetric products and the update run in 256x256 tiles (ragged
+# long sides padded inside the tiles); 1152 keeps the 128-wide tiles.
+BIG_SHAPES = [(1024, 1100), (1100, 1024), (1280, 1536), (1152, 1200)]
+
+
+@pytest.mark.parametrize("shape", BIG_SHAPES)
+@pytest.mark.parametrize("variant,stats", [("muon", True), ("muongs", True), ("muon", False)])
+def test_bf16_large_tiles(shape, variant, stats):
+    W, G, M = inputs(*shape, torch.bfloat16, seed=shape[0] + 7 * shape[1], m_std=1e-3)
+    W1, M1, st = gpu_step(W, G, M, stats=stats, variant=variant)
+    e, _, _ = check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st)
+    print(f"bf16 {shape} {variant} stats={stats}: relF(dW) = {e:.2e}")
+
+
 # Plain Muon without statistics: on the bf16 path the last Newton-Schulz
 # update applies the step to W itself whenever the weight's row length is a
 # multiple of 8 (the other shapes here take the separate tail).

@@ -138,25 +138,18 @@ int check_group(const muon_group& g, int dtype) {
 struct PhaseTiles {
   int64_t head, gram, update, tail;
 };
-// bf16 matrices whose symmetric products take the 256x256 tiles.
-bool syrk_big(const Layout& L, bool bf16) {
-  return bf16 && L.p >= kSyrkBigMinP && L.p_pad % kSyrkBigTile == 0;
-}
-bool upd_big(const Layout& L, bool bf16) {
-  return syrk_big(L, bf16) && L.q_pad % kUpdBigTile == 0;
+// bf16 matrices that may take 256x256 tiles (whether they do depends on the
+// launch: see the tile lists in run_groups).
+bool big_eligible(const Layout& L, bool bf16) {
+  return bf16 && L.p >= kBigMinP && L.p_pad % kBigTile == 0 && L.q_pad % kBigTile == 0;
 }
 PhaseTiles phase_tiles(const Layout& L, bool bf16) {
   PhaseTiles t;
-  const int64_t ts = bf16 ? (syrk_big(L, bf16) ? kSyrkBigTile : kSyrkTile) : kF32Tile;
+  const int64_t ts = bf16 ? kSyrkTile : kF32Tile;
   const int64_t nt = L.p_pad / ts;
   t.head = L.head_tiles;
   t.gram = nt * (nt + 1) / 2;
-  if (!bf16)
-    t.update = (L.p_pad / kF32Tile) * (L.q_pad / kF32Tile);
-  else if (upd_big(L, bf16))
-    t.update = (L.p_pad / kUpdBigTile) * (L.q_pad / kUpdBigTile);
-  else
-    t.update = (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN);
+  t.update = bf16 ? (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN) : nt * (L.q_pad / kF32Tile);
   t.tail = L.tail_tiles;
   return t;
 }
@@ -421,23 +414,39 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
         g_last_hip_error = int(hipErrorInvalidDevice);
         return MUON_ERR_HIP;
       }
+      // 256x256 tiles where the launch has enough of them: measured, they
+      // are faster on a GPT-400M model (short side 1024) and on MoE experts
+      // (512), slower on GPT-160M (768: 1.7 rounds of symmetric tiles, 5 of
+      // update tiles).
+      int64_t big_syrk = 0, big_upd = 0;
+      for (int k = 0; k < nsel; ++k) {
+        if (!big_eligible(sel[k].L, true)) continue;
+        const int64_t nb = sel[k].L.p_pad / kBigTile;
+        big_syrk += bt.g[k].count * (nb * (nb + 1) / 2);
+        big_upd += bt.g[k].count * nb * (sel[k].L.q_pad / kBigTile);
+      }
+      const bool use_big_syrk = big_syrk >= int64_t(kSyrkBigMinRounds) * 8 * cpx;
+      const bool use_big_upd = big_upd >= int64_t(kUpdBigMinRounds) * 8 * cpx;
       int64_t nt[kMaxGroups], ntb[kMaxGroups], nu[kMaxGroups], nub[kMaxGroups], kq[kMaxGroups],
           kp[kMaxGroups];
       for (int k = 0; k < nsel; ++k) {
-        const bool big = syrk_big(sel[k].L, true), ubig = upd_big(sel[k].L, true);
+        const Layout& L = sel[k].L;
+        const bool elig = big_eligible(L, true);
+        const bool big = use_big_syrk && elig, ubig = use_big_upd && elig;
+        const int64_t nb = L.p_pad / kBigTile;
         nt[k] = big ? 0 : w_gram.tiles[k];
-        ntb[k] = big ? w_gram.tiles[k] : 0;
+        ntb[k] = big ? nb * (nb + 1) / 2 : 0;
         nu[k] = ubig ? 0 : w_upd.tiles[k];
-        nub[k] = ubig ? w_upd.tiles[k] : 0;
+        nub[k] = ubig ? nb * (L.q_pad / kBigTile) : 0;
         kq[k] = bt.g[k].q_pad;
         kp[k] = bt.g[k].p_pad;
       }
       tl_gram = make_tile_list(bt, nt, kq, kSyrkBlocksPerCU * cpx);
       tl_poly = make_tile_list(bt, nt, kp, kSyrkBlocksPerCU * cpx);
-      tl_gram_big = make_tile_list(bt, ntb, kq, kSyrkBigBlocksPerCU * cpx);
-      tl_poly_big = make_tile_list(bt, ntb, kp, kSyrkBigBlocksPerCU * cpx);
+      tl_gram_big = make_tile_list(bt, ntb, kq, kBigBlocksPerCU * cpx);
+      tl_poly_big = make_tile_list(bt, ntb, kp, kBigBlocksPerCU * cpx);
       tl_upd = make_tile_list(bt, nu, kp, kUpdBlocksPerCU * cpx);
-      tl_upd_big = make_tile_list(bt, nub, kp, kUpdBigBlocksPerCU * cpx);
+      tl_upd_big = make_tile_list(bt, nub, kp, kBigBlocksPerCU * cpx);
     }
     hipEvent_t t0 = nullptr;
     Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};

@@ -53,17 +53,20 @@ constexpr int kUpdBlocksPerCU = kUpdWaves == 8 ? 1 : 2;
 #endif
 constexpr int kSyrkBlocksPerCU = MUON_SYRK_OCC;
 constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
-// Large matrices (short side at least kSyrkBigMinP, padded short side a
-// multiple of kSyrkBigTile) take the symmetric products in 256x256 tiles.
+// 256x256 tiles (8 waves, one block per CU) for matrices whose short side
+// is at least kBigMinP and whose padded sides are multiples of 256, in a
+// launch that then holds at least kSyrkBigMinRounds (symmetric products) or
+// kUpdBigMinRounds (update) tiles per CU; otherwise the 128-wide tiles.
 #ifndef MUON_SYRK_BIG_MIN_P
-#define MUON_SYRK_BIG_MIN_P 1024
+#define MUON_SYRK_BIG_MIN_P 512
 #endif
-constexpr int kSyrkBigTile = 256;
-constexpr int kSyrkBigMinP = MUON_SYRK_BIG_MIN_P;
-constexpr int kSyrkBigBlocksPerCU = 1;
-// ... and their update in 256x256 tiles (one block per CU).
-constexpr int kUpdBigTile = 256;
-constexpr int kUpdBigBlocksPerCU = 1;
+constexpr int kBigTile = 256;
+constexpr int kBigMinP = MUON_SYRK_BIG_MIN_P;
+constexpr int kBigBlocksPerCU = 1;
+constexpr int kSyrkBigMinRounds = 4;
+constexpr int kUpdBigMinRounds = 8;
+constexpr int kSyrkBigTile = kBigTile;
+constexpr int kUpdBigTile = kBigTile;
 constexpr int kUpdTileM = MUON_UPD_TILE_M;  // update: rows (along p)
 constexpr int kUpdTileN = MUON_UPD_TILE_N;  // update: columns (along q)
 constexpr int kBf16PadP = kSyrkTile > kUpdTileM ? kSyrkTile : kUpdTileM;

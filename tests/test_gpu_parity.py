@@ -81,19 +81,47 @@ def test_bf16_ragged(shape, variant):
     print(f"bf16 {shape} {variant}: relF(dW) = {e:.2e}")
 
 
-# Short side of at least 1024 with a padded short side that is a multiple of
-# 256: the symmetric products and the update run in 256x256 tiles (ragged
-# long sides padded inside the tiles); 1152 keeps the 128-wide tiles.
-BIG_SHAPES = [(1024, 1100), (1100, 1024), (1280, 1536), (1152, 1200)]
-
-
-@pytest.mark.parametrize("shape", BIG_SHAPES)
+# 256x256 tiles: matrices whose short side is at least 512 and whose padded
+# sides are multiples of 256, in a launch holding at least 4 (symmetric
+# products) and 8 (update) such tiles per CU.  Here 110 matrices of
+# 1024x1100 (10 symmetric and 20 update tiles each, ragged long side) next
+# to a group of 1152x1200, whose padded short side keeps the 128-wide tiles:
+# each phase then runs as two launches, read off the library's launch count.
 @pytest.mark.parametrize("variant,stats", [("muon", True), ("muongs", True), ("muon", False)])
-def test_bf16_large_tiles(shape, variant, stats):
-    W, G, M = inputs(*shape, torch.bfloat16, seed=shape[0] + 7 * shape[1], m_std=1e-3)
-    W1, M1, st = gpu_step(W, G, M, stats=stats, variant=variant)
-    e, _, _ = check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st)
-    print(f"bf16 {shape} {variant} stats={stats}: relF(dW) = {e:.2e}")
+def test_bf16_large_tiles(variant, stats):
+    import ctypes
+    from muon_step_03_amd import _lib
+    shapes = [(110, 1024, 1100), (3, 1152, 1200)]
+    Ws = [wl.random_matrix(c * r, k, 0.02, 900 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(shapes)]
+    Gs = [wl.random_matrix(c * r, k, 1e-3, 910 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(shapes)]
+    Ms = [wl.random_matrix(c * r, k, 1e-3, 920 + i, torch.float32, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(shapes)]
+    picks = [(0, 0), (0, 57), (0, 109), (1, 2)]
+    before = {pk: (Ws[pk[0]][pk[1]].clone(), Ms[pk[0]][pk[1]].clone()) for pk in picks}
+    st = torch.zeros(113 * 5, device=DEV) if stats else None
+    L = _lib.lib()
+    n = _lib.MUON_NUM_PHASES
+    ms, cnt = (ctypes.c_double * n)(), (ctypes.c_int64 * n)()
+    assert L.muon_profile_read(ms, cnt, n) == 0      # drop earlier records
+    ms, cnt = (ctypes.c_double * n)(), (ctypes.c_int64 * n)()
+    L.muon_profile_enable(1)
+    muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Ws, Gs, Ms)], torch.bfloat16,
+                      variant=variant, stats=st, **HP)
+    torch.cuda.synchronize()
+    L.muon_profile_enable(0)
+    assert L.muon_profile_read(ms, cnt, n) == 0
+    names = [L.muon_phase_name(i).decode() for i in range(n)]
+    launches = {names[i]: cnt[i] for i in range(n)}
+    assert launches["gram"] == 10 and launches["poly"] == 10, launches
+    assert launches["update"] + launches["update_tail"] == 10, launches
+    for gi, i in picks:
+        W0, M0 = before[(gi, i)]
+        s5 = st[(110 * gi + i) * 5:(110 * gi + i + 1) * 5] if stats else None
+        e, _, _ = check_against_oracle(W0, Gs[gi][i], M0, Ws[gi][i], Ms[gi][i], variant=variant,
+                                       stats=s5)
+        print(f"bf16 {shapes[gi][1:]} #{i} {variant} stats={stats}: relF(dW) = {e:.2e}")
 
 
 # Plain Muon without statistics: on the bf16 path the last Newton-Schulz

@@ -246,18 +246,21 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     Pa = Xin + i0 * qp;
     Pb = Xin + j0 * qp;
     lda = ldb = qp;
-    K = g.q_pad;
+    // X's padding columns (q .. q_pad) hold zeros: the contraction stops at
+    // the first K step boundary past q (and past p below, for A and B,
+    // whose padding rows and columns are zero as well)
+    K = (g.q + BK - 1) / BK * BK;
   } else if (MODE == MODE_POLY) {
     Pa = Am + i0 * pp;
     Pb = Am + j0 * pp;
     lda = ldb = pp;
-    K = g.p_pad;
+    K = (g.p + BK - 1) / BK * BK;
   } else {
     Pa = Bm + i0 * pp;
     lda = pp;
     Pb = Xin + j0;
     ldb = qp;
-    K = g.p_pad;
+    K = (g.p + BK - 1) / BK * BK;
   }
   const int nk = K / BK;
 

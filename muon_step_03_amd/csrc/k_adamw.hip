@@ -37,24 +37,34 @@ __device__ __forceinline__ float adam_elem(float p, float g, float& m, float& v,
   return __builtin_fmaf(c.decay, p, -(c.step_size * (m / denom)));
 }
 
+// Every stream is read and written once per step: nontemporal accesses
+// (evict-first in the caches).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <bool BF16>
 __device__ __forceinline__ f32x4 load4(const void* base, int64_t e) {
   if constexpr (BF16) {
-    const u16x4 h = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(base) + e);
+    const u16x4 h = __builtin_nontemporal_load(
+        reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(base) + e));
     return f32x4{bf2f(h.x), bf2f(h.y), bf2f(h.z), bf2f(h.w)};
   } else {
-    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + e);
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + e));
   }
 }
 
 template <bool BF16>
 __device__ __forceinline__ void store4(void* base, int64_t e, f32x4 x) {
   if constexpr (BF16) {
-    const uint32_t lo = f2bf2(x.x, x.y), hi = f2bf2(x.z, x.w);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + e) = make_uint2(lo, hi);
+    const u32x2 w = {f2bf2(x.x, x.y), f2bf2(x.z, x.w)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + e));
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + e) = x;
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(static_cast<float*>(base) + e));
   }
+}
+__device__ __forceinline__ f32x4 load4f(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void store4f(float* p, f32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
 template <bool BF16>
@@ -75,8 +85,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamBatch bt) {
       const int64_t e = base + int64_t(j * 256 + t) * kAdamVec;
       p[j] = load4<BF16>(sg.P, e);
       g[j] = load4<BF16>(sg.G, e);
-      m[j] = *reinterpret_cast<const f32x4*>(sg.m + e);
-      v[j] = *reinterpret_cast<const f32x4*>(sg.v + e);
+      m[j] = load4f(sg.m + e);
+      v[j] = load4f(sg.v + e);
     }
 #pragma unroll
     for (int j = 0; j < kAdamVecPerThread; ++j) {
@@ -90,8 +100,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamBatch bt) {
         v[j][k] = vk;
       }
       store4<BF16>(sg.P, e, r);
-      *reinterpret_cast<f32x4*>(sg.m + e) = m[j];
-      *reinterpret_cast<f32x4*>(sg.v + e) = v[j];
+      store4f(sg.m + e, m[j]);
+      store4f(sg.v + e, v[j]);
     }
     return;
   }

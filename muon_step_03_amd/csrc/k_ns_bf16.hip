@@ -17,9 +17,13 @@
 // ||U|| while it writes X0): its Gram is scaled by inv^2 and its update by
 // inv, inv = 1/(||U||_F + 1e-7), which is the iteration applied to U*inv.
 //
-// Kernel structure (defaults: 256 threads = 4 waves in a 2x2 grid):
-//  * Block tiles are compile-time (defaults: symmetric products 128x128,
-//    64x64 per wave; update 128x256, 64x128 per wave).
+// Kernel structure (one template, three configurations per product):
+//  * Block tiles are compile-time: symmetric products 128x128 (4 waves of
+//    64x64, two blocks per CU), update 128x256 (4 waves of 64x128, two
+//    blocks per CU), and for large matrices 256x256 for both (8 waves of
+//    128x64, one block per CU).  A CU moves at most about 64 bytes per clock
+//    from L2 into LDS, which is what a 128x128 tile needs to keep its matrix
+//    cores busy; the larger tiles need half as much per flop.
 //  * K steps of 32, staged through LDS by 16-byte direct-to-LDS loads
 //    (global_load_lds): STAGES buffers, loads for up to STAGES-1 later steps
 //    in flight while step k is multiplied; one barrier per K step, and the
@@ -44,7 +48,7 @@
 //    ds_read_b64_tr_b16: within a 16-lane group, output lane i element j
 //    comes from source lane 4j + i/4, element i%4, so lane s addresses
 //    X[k0 + s/4][n0 + 4 (s%4)] and two reads give 8 consecutive k.
-//  * Persistent blocks (two per CU) walk a static tile list: XCD x (the
+//  * Persistent blocks walk a static tile list: XCD x (the
 //    hardware dispatches block b to XCD b % 8) takes one contiguous eighth of
 //    every group's tiles, so its blocks work on consecutive tiles of one
 //    matrix at a time and share its operands in that XCD's L2; a block's

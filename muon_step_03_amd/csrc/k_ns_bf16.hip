@@ -381,6 +381,45 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // every wave) becomes readable.  The loop is unrolled by S so that every
   // stage buffer index is a compile-time constant.
   bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
+  if constexpr (C::NW == 8) {
+  // Eight waves, two per SIMD: the waves 0-3 and 4-7 run half a K step
+  // apart, so that on every SIMD one wave issues its MFMAs while the other
+  // reads its next fragments from LDS and issues its loads.  Each K step is
+  // a memory phase (fragments of both 16-deep sub-steps, the loads of step
+  // kt+S-1 into the buffer step kt-1 used) and a compute phase (all MFMAs of
+  // the step), each closed by a barrier; the second group enters the loop
+  // one barrier late and the first leaves it one barrier late, so both pass
+  // the same barriers.  Between consecutive barriers one group reads and
+  // loads while the other multiplies.  Step kt+1 is complete before the
+  // barrier after which the first group reads it: each wave waits for its
+  // own loads of it at the end of its phase before that barrier.
+  const bool late = wave >= 4;
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
+  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, 2);
+  wait_stage(0, S - 2);  // the prologue issued steps 0 .. S-2
+  block_barrier();
+  if (late) block_barrier();
+  auto pp = [&](auto bufc, int kt) {
+    constexpr int J = decltype(bufc)::value;
+    load_frags(bufc, 0, a0, b0);
+    load_frags(bufc, 1, a1, b1);
+    if (kt + S - 1 < nk) issue(std::integral_constant<int, (J + S - 1) % S>{}, kt + S - 1);
+    if (late && kt + 1 < nk) wait_stage(kt + 1, kt + S - 1);
+    block_barrier();
+    mfmas(a0, b0);
+    mfmas(a1, b1);
+    if (!late && kt + 1 < nk) wait_stage(kt + 1, kt + S - 1);
+    block_barrier();
+  };
+  for (int kt = 0; kt < nk; kt += S) {
+    pp(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) pp(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (S > 2) if (kt + 2 < nk) pp(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, kt + 2);
+    if constexpr (S > 3) if (kt + 3 < nk) pp(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, kt + 3);
+  }
+  if (!late) block_barrier();
+  } else {
   issue(std::integral_constant<int, 0>{}, 0);
   if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
   if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, 2);
@@ -405,6 +444,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
     if constexpr (S > 2) if (kt + 2 < nk) step(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, kt + 2);
     if constexpr (S > 3) if (kt + 3 < nk) step(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, kt + 3);
+  }
   }
 
   // ---- Epilogue: the final fp32 tile is staged through LDS in two passes

@@ -63,8 +63,14 @@ constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
 constexpr int kBigTile = 256;
 constexpr int kBigMinP = MUON_SYRK_BIG_MIN_P;
 constexpr int kBigBlocksPerCU = 1;
-constexpr int kSyrkBigMinRounds = 4;
-constexpr int kUpdBigMinRounds = 8;
+#ifndef MUON_SYRK_BIG_MIN_ROUNDS
+#define MUON_SYRK_BIG_MIN_ROUNDS 4
+#endif
+#ifndef MUON_UPD_BIG_MIN_ROUNDS
+#define MUON_UPD_BIG_MIN_ROUNDS 8
+#endif
+constexpr int kSyrkBigMinRounds = MUON_SYRK_BIG_MIN_ROUNDS;
+constexpr int kUpdBigMinRounds = MUON_UPD_BIG_MIN_ROUNDS;
 constexpr int kSyrkBigTile = kBigTile;
 constexpr int kUpdBigTile = kBigTile;
 constexpr int kUpdTileM = MUON_UPD_TILE_M;  // update: rows (along p)

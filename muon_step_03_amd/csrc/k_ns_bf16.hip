@@ -599,16 +599,36 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       for (int e = 0; e < 8; ++e) wp[e] = f2bf(fmaf(dec, bf2f(wp[e]), -stp * o[e]));
     }
   };
+  // W' chunk from a W chunk loaded beforehand.
+  auto w_apply = [&](const uint4& w, const float (&o)[8]) {
+    const float dec = g.decay, stp = g.step;
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = fmaf(dec, __uint_as_float(ww[e] << 16), -stp * o[2 * e]);
+      v[2 * e + 1] = fmaf(dec, __uint_as_float(ww[e] & 0xffff0000u), -stp * o[2 * e + 1]);
+    }
+    return pack8(v);
+  };
   auto finish_tail = [&](int pass) {
     uint16_t* Wm = mat_ptr<uint16_t>(g.W_tab, g.W, m, int64_t(g.rows) * g.cols);
     const int64_t wld = g.cols;
     const bool wvec = (reinterpret_cast<uintptr_t>(Wm) & 15) == 0;
-    uint4 lin[CHUNKS];
+    // 16-byte W chunks of the pass, all loaded before the first W' store
+    // (which the compiler may not move loads across) so that their latencies
+    // overlap: by rows for a wide W, by columns (after the barrier) for a tall
+    // one.
+    uint4 lin[CHUNKS], wv[CHUNKS];
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int q = t + NT * u;
       const int row = q / CPR, col = (q % CPR) * 8;
       lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
+      const int i = i0 + 64 * pass + row, j = j0 + col;
+      wv[u] = make_uint4(0, 0, 0, 0);
+      if (!g.trans && wvec && i < g.p && j < g.q)
+        wv[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(i) * wld + j);
     }
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
@@ -625,7 +645,13 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       add_lin(v, lin[u]);
       const int i = i0 + 64 * pass + row, j = j0 + col;
       if (!g.trans) {
-        if (i < g.p && j < g.q) w_update(Wm + int64_t(i) * wld + j, wvec, v);
+        if (i < g.p && j < g.q) {
+          uint16_t* wp = Wm + int64_t(i) * wld + j;
+          if (wvec)
+            *reinterpret_cast<uint4*>(wp) = w_apply(wv[u], v);
+          else
+            w_update(wp, false, v);
+        }
       } else {
         // O is needed by columns: keep the complete values in T
         *(LDS_AS f32x4_t*)(T + row * TP + col) = f32x4_t{v[0], v[1], v[2], v[3]};
@@ -633,10 +659,20 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       }
     }
     if (g.trans) {
-      block_barrier();
+      constexpr int MC = BN * 8 / NT;
       // W row j0 + c, columns i0 + 64 pass + r8 .. +7, from staged column c
+      uint4 wt[MC];
 #pragma unroll
-      for (int u = 0; u < BN * 8 / NT; ++u) {
+      for (int u = 0; u < MC; ++u) {
+        const int q = t + NT * u;
+        const int c = q % BN, r8 = (q / BN) * 8;
+        const int i = i0 + 64 * pass + r8, j = j0 + c;
+        wt[u] = make_uint4(0, 0, 0, 0);
+        if (wvec && j < g.q && i < g.p) wt[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(j) * wld + i);
+      }
+      block_barrier();
+#pragma unroll
+      for (int u = 0; u < MC; ++u) {
         const int q = t + NT * u;
         const int c = q % BN, r8 = (q / BN) * 8;
         const int i = i0 + 64 * pass + r8, j = j0 + c;
@@ -644,7 +680,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
-        w_update(Wm + int64_t(j) * wld + i, wvec, v);
+        uint16_t* wp = Wm + int64_t(j) * wld + i;
+        if (wvec)
+          *reinterpret_cast<uint4*>(wp) = w_apply(wt[u], v);
+        else
+          w_update(wp, false, v);
       }
     }
   };

@@ -67,15 +67,20 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BK = 32;
 constexpr int WAVE_BYTES = 1024;    // bytes one direct-to-LDS instruction moves
 
 enum { MODE_GRAM = 0, MODE_POLY = 1, MODE_UPDATE = 2 };
 
 template <int MODE>
 struct Cfg;
+// Symmetric products: K step of 64 (operand rows of 128 bytes, whole cache
+// lines: a CU's load path moves rows of 64 bytes at half the rate, 31 vs 60
+// bytes per clock measured), two stages of 32 KiB.
+#ifndef MUON_SYRK_BK
+#define MUON_SYRK_BK 64
+#endif
 #ifndef MUON_SYRK_STAGES
-#define MUON_SYRK_STAGES 4
+#define MUON_SYRK_STAGES (MUON_SYRK_BK == 64 ? 2 : 4)
 #endif
 #ifndef MUON_UPD_STAGES
 #define MUON_UPD_STAGES 3
@@ -90,6 +95,7 @@ template <>
 struct Cfg<MODE_GRAM> {
   static constexpr int BM = kSyrkTile, BN = kSyrkTile, NW = 4, WGM = 2, WGN = 2;
   static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int BK = MUON_SYRK_BK;
   static constexpr int STAGES = MUON_SYRK_STAGES;
   static constexpr int OCC = kSyrkBlocksPerCU;
 };
@@ -102,6 +108,7 @@ struct Cfg<MODE_POLY> : Cfg<MODE_GRAM> {};
 struct CfgSyrkBig {
   static constexpr int BM = kSyrkBigTile, BN = kSyrkBigTile, NW = 8, WGM = 2, WGN = 4;
   static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int BK = 32;
   static constexpr int STAGES = 4;
   static constexpr int OCC = 1;
 };
@@ -110,6 +117,7 @@ struct CfgSyrkBig {
 struct CfgUpdBig {
   static constexpr int BM = kUpdBigTile, BN = kUpdBigTile, NW = 8, WGM = 2, WGN = 4;
   static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int BK = 32;
   static constexpr int STAGES = 4;
   static constexpr int OCC = 1;
 };
@@ -118,11 +126,22 @@ struct Cfg<MODE_UPDATE> {
   static constexpr int BM = kUpdTileM, BN = kUpdTileN, NW = kUpdWaves, WGM = MUON_UPD_WGM,
                        WGN = NW / WGM;
   static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int BK = 32;
   static constexpr int STAGES = MUON_UPD_STAGES;
   static constexpr int OCC = kUpdBlocksPerCU;
 };
 
 __device__ __forceinline__ int fswz(int m) { return ((m >> 1) + (m >> 3)) & 3; }
+// Row swizzle of K-contiguous tiles: 4 chunks of 16 B per row (K step 32),
+// or 8 chunks (K step 64: rows r and r+1 fill one 256-byte bank window, so
+// (r >> 1) & 7 spreads 16 consecutive rows over 16 distinct slots).
+template <int CPR>
+__device__ __forceinline__ int rswz(int m) {
+  if constexpr (CPR == 4)
+    return fswz(m);
+  else
+    return (m >> 1) & 7;
+}
 __device__ __forceinline__ int gswz(int k) { return (0xACE0 >> ((k & 3) * 4)) & 15; }  // {0,6,12,10}
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima).
@@ -169,8 +188,10 @@ __device__ __forceinline__ void tri_decode(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
+template <int BK>
 __device__ __forceinline__ bf16x8_t lds_frag_rows(const LDS_AS char* tile, int row, int chunk) {
-  return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * (BK * 2) + ((chunk ^ fswz(row)) << 4));
+  return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * (BK * 2) +
+                                                   ((chunk ^ rswz<BK / 8>(row)) << 4));
 }
 
 template <int BN>
@@ -189,7 +210,11 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
 template <int MODE, class C>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     Batch bt, TileList tl, int iter, float c1, float c2) {
-  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES;
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES, BK = C::BK;
+  constexpr int KS = BK / 16;                        // MFMA sub-steps per K step
+  constexpr int CPK = BK / 8;                        // 16-byte chunks per operand row
+  static_assert(KS == 2 || KS == 4, "K step of 32 or 64");
+  static_assert(MODE != MODE_UPDATE || BK == 32, "the update's X tile has 32 K-rows");
   constexpr int NT = 64 * C::NW;                     // threads per block
   constexpr int A_BYTES = BM * BK * 2;
   constexpr int B_BYTES = BN * BK * 2;
@@ -284,8 +309,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   uint32_t offA[A_INSTR], offB[B_INSTR];
 #pragma unroll
   for (int i = 0; i < A_INSTR; ++i) {
-    const int row = (wave * A_INSTR + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ fswz(row);
+    // one instruction: 64/CPK rows of CPK 16-byte chunks (whole rows)
+    const int row = (wave * A_INSTR + i) * (64 / CPK) + lane / CPK;
+    const int c = (lane % CPK) ^ rswz<CPK>(row);
     offA[i] = uint32_t((int64_t(row) * lda + c * 8) * 2);
   }
 #pragma unroll
@@ -297,8 +323,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       const int c = (lane % CPR) ^ gswz(k);
       offB[i] = uint32_t((int64_t(k) * ldb + c * 8) * 2);
     } else {
-      const int row = (wave * B_INSTR + i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ fswz(row);
+      const int row = (wave * B_INSTR + i) * (64 / CPK) + lane / CPK;
+      const int c = (lane % CPK) ^ rswz<CPK>(row);
       offB[i] = uint32_t((int64_t(row) * ldb + c * 8) * 2);
     }
   }
@@ -337,13 +363,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     const LDS_AS char* sB = smem + S * A_BYTES + J * B_BYTES;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int mi = 0; mi < WM; ++mi) af[mi] = lds_frag_rows(sA, wm * 32 * WM + mi * 32 + (lane & 31), ch);
+    for (int mi = 0; mi < WM; ++mi)
+      af[mi] = lds_frag_rows<BK>(sA, wm * 32 * WM + mi * 32 + (lane & 31), ch);
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni) {
       if (MODE == MODE_UPDATE)
         bfr[ni] = lds_frag_xT<BN>(sB, ks * 16, wn * 32 * WN + ni * 32, lane);
       else
-        bfr[ni] = lds_frag_rows(sB, wn * 32 * WN + ni * 32 + (lane & 31), ch);
+        bfr[ni] = lds_frag_rows<BK>(sB, wn * 32 * WN + ni * 32 + (lane & 31), ch);
     }
   };
   // The B fragment goes in the MFMA's first operand slot: the accumulator
@@ -373,11 +400,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   };
   static_assert(S >= 2 && S <= 4, "wait_stage covers at most 3 younger stages");
 
-  // Software pipeline over K steps (two 16-deep sub-steps each): the LDS
+  // Software pipeline over K steps (KS 16-deep sub-steps each): the LDS
   // reads of the next sub-step are always in flight while the MFMAs of the
-  // current one issue.  One barrier per K step, between its sub-steps: all
-  // reads of step kt are complete there (lgkmcnt 0), so its buffer is
-  // refilled with step kt+S right after it, and step kt+1 (waited for by
+  // current one issue.  One barrier per K step, before its last sub-step's
+  // MFMAs: all reads of step kt are complete there (lgkmcnt 0), so its buffer
+  // is refilled with step kt+S right after it, and step kt+1 (waited for by
   // every wave) becomes readable.  The loop is unrolled by S so that every
   // stage buffer index is a compile-time constant.
   bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
@@ -400,6 +427,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   wait_stage(0, S - 2);  // the prologue issued steps 0 .. S-2
   block_barrier();
   if (late) block_barrier();
+  static_assert(KS == 2, "the ping-pong loop holds the fragments of one 32-deep K step");
   auto pp = [&](auto bufc, int kt) {
     constexpr int J = decltype(bufc)::value;
     load_frags(bufc, 0, a0, b0);
@@ -431,6 +459,12 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     constexpr int J = decltype(bufc)::value;
     load_frags(bufc, 1, a1, b1);
     mfmas(a0, b0);
+    if constexpr (KS == 4) {
+      load_frags(bufc, 2, a0, b0);
+      mfmas(a1, b1);
+      load_frags(bufc, 3, a1, b1);
+      mfmas(a0, b0);
+    }
     if (kt + 1 < nk) {
       wait_stage(kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
       block_barrier();

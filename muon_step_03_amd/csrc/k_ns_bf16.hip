@@ -68,6 +68,7 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int WAVE_BYTES = 1024;    // bytes one direct-to-LDS instruction moves
+constexpr int kPanel = 32;          // column panel width of the stored B
 
 enum { MODE_GRAM = 0, MODE_POLY = 1, MODE_UPDATE = 2 };
 
@@ -285,8 +286,10 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     lda = ldb = pp;
     K = (g.p + BK - 1) / BK * BK;
   } else {
-    Pa = Bm + i0 * pp;
-    lda = pp;
+    // B is stored in panels of 32 columns ([p/32][p][32]): the 128 rows of
+    // one K step are 8 contiguous KiB, loaded as whole cache lines
+    Pa = Bm + i0 * kPanel;
+    lda = kPanel;
     Pb = Xin + j0;
     ldb = qp;
     K = (g.p + BK - 1) / BK * BK;
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   }
   const char* gA = reinterpret_cast<const char*>(Pa);
   const char* gB = reinterpret_cast<const char*>(Pb);
-  const int64_t stepA = BK * 2;
+  const int64_t stepA = MODE == MODE_UPDATE ? pp * kPanel * 2 : BK * 2;
   const int64_t stepB = MODE == MODE_UPDATE ? int64_t(BK) * ldb * 2 : int64_t(BK) * 2;
 
   // Issue the loads of K step `kt` into stage buffer J (= kt % S).  Each wave
@@ -511,6 +514,15 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   constexpr int CHUNKS = 64 * CPR / NT;      // per thread per pass
   uint16_t* Cout = MODE == MODE_UPDATE ? Xout : (MODE == MODE_GRAM ? Am : Bm);
   const int64_t ldc = MODE == MODE_UPDATE ? qp : pp;
+  // Output element (r, c): row-major, except the polynomial's B, which the
+  // update reads in panels of 32 columns (8 aligned columns stay contiguous).
+  auto out_at = [&](int64_t r, int64_t c) -> uint16_t* {
+    if constexpr (MODE == MODE_POLY)
+      return Cout + (c / kPanel) * (pp * kPanel) + r * kPanel + (c % kPanel);
+    else
+      return Cout + r * ldc + c;
+  };
+
 
   // Pass `pass` stages tile rows 64 pass .. +63: the 32-row accumulator
   // blocks wm*WM + mi with (wm*WM + mi) / 2 == pass.
@@ -588,7 +600,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         v[e + 4] = v1[e];
       }
       if (kLin) add_lin(v, lin[u]);
-      *reinterpret_cast<uint4*>(Cout + (i0 + 64 * pass + row) * ldc + j0 + col) = pack8(v);
+      *reinterpret_cast<uint4*>(out_at(i0 + 64 * pass + row, j0 + col)) = pack8(v);
     }
     if (mirror) {
       // Mirrored block: rows j0 + c of C (c < BN), columns i0 + 64*pass + r8
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
         if (kLin) add_lin(v, lin_m[u]);
-        *reinterpret_cast<uint4*>(Cout + (j0 + c) * ldc + i0 + 64 * pass + r8) = pack8(v);
+        *reinterpret_cast<uint4*>(out_at(j0 + c, i0 + 64 * pass + r8)) = pack8(v);
       }
     }
   };

@@ -106,11 +106,14 @@ struct Cfg<MODE_POLY> : Cfg<MODE_GRAM> {};
 // one block per CU (four stages of 32 KiB).  Every operand byte brought into
 // a CU feeds twice the MFMA work of a 128x128 tile, which halves the L2 and
 // fabric traffic of the long-K Gram products of wide matrices.
+#ifndef MUON_SYRK_BIG_BK
+#define MUON_SYRK_BIG_BK 32
+#endif
 struct CfgSyrkBig {
   static constexpr int BM = kSyrkBigTile, BN = kSyrkBigTile, NW = 8, WGM = 2, WGN = 4;
   static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
-  static constexpr int BK = 32;
-  static constexpr int STAGES = 4;
+  static constexpr int BK = MUON_SYRK_BIG_BK;
+  static constexpr int STAGES = BK == 64 ? 2 : 4;
   static constexpr int OCC = 1;
 };
 // Update of large matrices: 256x256 tiles, 8 waves of 128x64, one block
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // every wave) becomes readable.  The loop is unrolled by S so that every
   // stage buffer index is a compile-time constant.
   bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
-  if constexpr (C::NW == 8) {
+  if constexpr (C::NW == 8 && KS == 2) {
   // Eight waves, two per SIMD: the waves 0-3 and 4-7 run half a K step
   // apart, so that on every SIMD one wave issues its MFMAs while the other
   // reads its next fragments from LDS and issues its loads.  Each K step is

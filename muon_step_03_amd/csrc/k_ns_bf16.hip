@@ -24,10 +24,16 @@
 //    128x64, one block per CU).  A CU moves at most about 64 bytes per clock
 //    from L2 into LDS, which is what a 128x128 tile needs to keep its matrix
 //    cores busy; the larger tiles need half as much per flop.
-//  * K steps of 32, staged through LDS by 16-byte direct-to-LDS loads
+//  * K steps of 64 (128-wide symmetric products) or 32 (update, 256x256
+//    tiles), staged through LDS by 16-byte direct-to-LDS loads
 //    (global_load_lds): STAGES buffers, loads for up to STAGES-1 later steps
 //    in flight while step k is multiplied; one barrier per K step, and the
-//    MFMA fragments double-buffered in registers.  The loads address memory
+//    MFMA fragments double-buffered in registers.  Every load instruction
+//    reads whole 128-byte lines (a CU loads rows of 64 bytes at half the
+//    rate): operand rows of 128 bytes, the update's X rows of 512 bytes, and
+//    the polynomial's output B stored in panels of 32 columns
+//    ([p/32][p][32]), so that one K step of the update's B operand is a
+//    contiguous block.  The loads address memory
 //    as a scalar base (advanced once per K step) plus a per-lane offset
 //    fixed for the tile, and the K loop is unrolled by STAGES so that every
 //    LDS address is a lane's base plus an immediate: the loop body issues
@@ -36,10 +42,10 @@
 //    stored as 16-byte rows of 8 bf16; the linear terms (a*X of the update,
 //    b*A of the polynomial) are read there as 16-byte rows of the operand
 //    (L2-resident), so the K loop carries nothing but the product.
-//  * K-contiguous operand tiles: rows of 32 bf16 (64 B, 4 chunks of 16 B),
-//    chunk c of row m stored at c ^ f(m), f(m) = ((m>>1) + (m>>3)) & 3,
-//    so the fragment reads (32 consecutive rows, one chunk) do not collide
-//    in 32- or 64-bank LDS.  The swizzle is applied by choosing which
+//  * K-contiguous operand tiles: rows of BK bf16 (4 or 8 chunks of 16 B),
+//    chunk c of row m stored at c ^ f(m), f(m) = ((m>>1) + (m>>3)) & 3 for
+//    4 chunks, (m>>1) & 7 for 8, so the fragment reads (32 consecutive rows,
+//    one chunk) do not collide in 32- or 64-bank LDS.  The swizzle is applied by choosing which
 //    global chunk each lane fetches (a direct-to-LDS load writes lane L's
 //    16 bytes at base + 16 L).
 //  * The update's X operand is N-contiguous: its tile is kept as 32 K-rows

@@ -552,6 +552,44 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         }
     }
   };
+  // Mirrored blocks of symmetric tiles: the pass's accumulators are staged a
+  // second time, transposed (Tt[c][r], c < BN tile columns, r < 64 rows of
+  // the pass), so that the mirrored rows are read as 16-byte vectors and
+  // written as whole 128-byte row runs.  Row pitch 68: the 16-byte reads of
+  // 8 lanes per row over two rows hit distinct banks.
+  // (The 8-wave 256x256 tiles read the mirrored block by columns from the
+  // normal staging instead: the second staging costs them more than the
+  // scattered stores; lanes then take consecutive c, so the column reads
+  // hit distinct banks.)
+  constexpr bool kStageT = C::NW == 4;
+  constexpr int TPT = 68;
+  static_assert(MODE == MODE_UPDATE || BN * TPT * 4 <= S * STAGE_BYTES, "transposed staging");
+  // Mirrored chunk q: tile column c (a row of the mirrored block), rows
+  // r8 .. r8+7 of the pass.
+  auto mirror_pos = [&](int q, int& c, int& r8) {
+    if constexpr (kStageT) {
+      c = q >> 3;
+      r8 = (q & 7) * 8;
+    } else {
+      c = q % BN;
+      r8 = (q / BN) * 8;
+    }
+  };
+  auto stage_t = [&](int pass) {
+#pragma unroll
+    for (int mi = 0; mi < WM; ++mi) {
+      const int blk = wm * WM + mi;
+      if ((blk >> 1) != pass) continue;
+      const int row = (blk & 1) * 32 + (lane & 31);
+#pragma unroll
+      for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = wn * 32 * WN + ni * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          T[col * TPT + row] = acc[mi][ni][r];
+        }
+    }
+  };
   auto pack8 = [](const float (&v)[8]) {
     uint32_t w[4];
 #pragma unroll
@@ -587,8 +625,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       if (mirror) {
 #pragma unroll
         for (int u = 0; u < MCH; ++u) {
-          const int q = t + NT * u;
-          const int c = q % BN, r8 = (q / BN) * 8;
+          int c, r8;
+          mirror_pos(t + NT * u, c, r8);
           lin_m[u] = *reinterpret_cast<const uint4*>(Lin + (j0 + c) * ldc + i0 + 64 * pass + r8);
         }
       }
@@ -611,20 +649,30 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       if (kLin) add_lin(v, lin[u]);
       *reinterpret_cast<uint4*>(out_at(i0 + 64 * pass + row, j0 + col)) = pack8(v);
     }
-    if (mirror) {
-      // Mirrored block: rows j0 + c of C (c < BN), columns i0 + 64*pass + r8
-      // .. +7, from staged column c; lanes take consecutive c, so the
-      // column reads hit distinct banks.
+  };
+  // Mirrored block: rows j0 + c of C (c < BN), columns i0 + 64*pass + r8 ..
+  // +7, from the transposed staging; 8 consecutive lanes cover the 64
+  // columns of one row (a whole 128-byte line per row and instruction).
+  auto finish_mirror = [&](int pass, const uint4 (&lin_m)[kLin ? MCH : 1]) {
 #pragma unroll
-      for (int u = 0; u < MCH; ++u) {
-        const int q = t + NT * u;
-        const int c = q % BN, r8 = (q / BN) * 8;
-        float v[8];
+    for (int u = 0; u < MCH; ++u) {
+      int c, r8;
+      mirror_pos(t + NT * u, c, r8);
+      float v[8];
+      if constexpr (kStageT) {
+        const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + c * TPT + r8);
+        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + c * TPT + r8 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = v0[e];
+          v[e + 4] = v1[e];
+        }
+      } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
-        if (kLin) add_lin(v, lin_m[u]);
-        *reinterpret_cast<uint4*>(out_at(j0 + c, i0 + 64 * pass + r8)) = pack8(v);
       }
+      if (kLin) add_lin(v, lin_m[u]);
+      *reinterpret_cast<uint4*>(out_at(j0 + c, i0 + 64 * pass + r8)) = pack8(v);
     }
   };
 
@@ -670,20 +718,23 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     uint16_t* Wm = mat_ptr<uint16_t>(g.W_tab, g.W, m, int64_t(g.rows) * g.cols);
     const int64_t wld = g.cols;
     const bool wvec = (reinterpret_cast<uintptr_t>(Wm) & 15) == 0;
-    // 16-byte W chunks of the pass, all loaded before the first W' store
-    // (which the compiler may not move loads across) so that their latencies
-    // overlap: by rows for a wide W, by columns (after the barrier) for a tall
-    // one.
-    uint4 lin[CHUNKS], wv[CHUNKS];
+    // The 8-wave tiles load all 16-byte W chunks of the pass before the
+    // first W' store (which the compiler may not move loads across) so that
+    // their latencies overlap: by rows for a wide W, by columns for a tall
+    // one.  The 4-wave update has no registers to spare for them.
+    constexpr bool kPreW = C::NW == 8;
+    uint4 lin[CHUNKS], wv[kPreW ? CHUNKS : 1];
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int q = t + NT * u;
       const int row = q / CPR, col = (q % CPR) * 8;
       lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
-      const int i = i0 + 64 * pass + row, j = j0 + col;
-      wv[u] = make_uint4(0, 0, 0, 0);
-      if (!g.trans && wvec && i < g.p && j < g.q)
-        wv[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(i) * wld + j);
+      if constexpr (kPreW) {
+        const int i = i0 + 64 * pass + row, j = j0 + col;
+        wv[u] = make_uint4(0, 0, 0, 0);
+        if (!g.trans && wvec && i < g.p && j < g.q)
+          wv[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(i) * wld + j);
+      }
     }
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
@@ -702,10 +753,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       if (!g.trans) {
         if (i < g.p && j < g.q) {
           uint16_t* wp = Wm + int64_t(i) * wld + j;
-          if (wvec)
-            *reinterpret_cast<uint4*>(wp) = w_apply(wv[u], v);
-          else
-            w_update(wp, false, v);
+          if constexpr (kPreW) {
+            if (wvec)
+              *reinterpret_cast<uint4*>(wp) = w_apply(wv[u], v);
+            else
+              w_update(wp, false, v);
+          } else {
+            w_update(wp, wvec, v);
+          }
         }
       } else {
         // O is needed by columns: keep the complete values in T
@@ -716,30 +771,36 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     if (g.trans) {
       constexpr int MC = BN * 8 / NT;
       // W row j0 + c, columns i0 + 64 pass + r8 .. +7, from staged column c
-      uint4 wt[MC];
+      uint4 wt[kPreW ? MC : 1];
+      if constexpr (kPreW) {
 #pragma unroll
-      for (int u = 0; u < MC; ++u) {
-        const int q = t + NT * u;
-        const int c = q % BN, r8 = (q / BN) * 8;
-        const int i = i0 + 64 * pass + r8, j = j0 + c;
-        wt[u] = make_uint4(0, 0, 0, 0);
-        if (wvec && j < g.q && i < g.p) wt[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(j) * wld + i);
+        for (int u = 0; u < MC; ++u) {
+          const int q = t + NT * u;
+          const int c = q % BN, r8 = (q / BN) * 8;
+          const int i = i0 + 64 * pass + r8, j = j0 + c;
+          wt[u] = make_uint4(0, 0, 0, 0);
+          if (wvec && j < g.q && i < g.p) wt[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(j) * wld + i);
+        }
       }
       block_barrier();
 #pragma unroll
       for (int u = 0; u < MC; ++u) {
         const int q = t + NT * u;
-        const int c = q % BN, r8 = (q / BN) * 8;
+        const int c = q % BN, r8 = (q / BN) * 8;  // consecutive lanes: distinct banks
         const int i = i0 + 64 * pass + r8, j = j0 + c;
         if (j >= g.q || i >= g.p) continue;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
         uint16_t* wp = Wm + int64_t(j) * wld + i;
-        if (wvec)
-          *reinterpret_cast<uint4*>(wp) = w_apply(wt[u], v);
-        else
-          w_update(wp, false, v);
+        if constexpr (kPreW) {
+          if (wvec)
+            *reinterpret_cast<uint4*>(wp) = w_apply(wt[u], v);
+          else
+            w_update(wp, false, v);
+        } else {
+          w_update(wp, wvec, v);
+        }
       }
     }
   };
@@ -760,6 +821,16 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     } else {
       if (!kEarlyLin) load_lin(pass, lin, lin_m);
       finish(pass, lin, lin_m);
+      if constexpr (MODE != MODE_UPDATE) {
+        if (mirror) {
+          if constexpr (kStageT) {
+            block_barrier();  // the row reads of T are done
+            stage_t(pass);
+            block_barrier();
+          }
+          finish_mirror(pass, lin_m);
+        }
+      }
     }
   }
   }  // tiles of group oi

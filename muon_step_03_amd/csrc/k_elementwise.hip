@@ -110,10 +110,15 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
 
   const TileRef tr = decode(bt, wk);
   const MatGroup& g = *tr.g;
-  const int ntj = g.q_pad / T;
+  // A wide matrix (X = U, no transpose) is taken in tiles of 16 rows x 256
+  // columns (row runs of 512 / 1024 bytes of G / M), a tall one in 64 x 64
+  // tiles transposed through LDS; both shapes give the same tile count.
+  const bool flat = !g.trans && (g.q_pad % (4 * T)) == 0;
+  const int TR = flat ? T / 4 : T, TC = flat ? 4 * T : T;
+  const int ntj = g.q_pad / TC;
   const int ti = tr.tile / ntj;
   const int tj = tr.tile - ti * ntj;
-  const int i0 = ti * T, j0 = tj * T;            // X-orientation origin
+  const int i0 = ti * TR, j0 = tj * TC;          // X-orientation origin
   const int sr0 = g.trans ? j0 : i0;             // weight-orientation origin
   const int sc0 = g.trans ? i0 : j0;
   const int64_t elems = int64_t(g.rows) * g.cols;
@@ -123,16 +128,19 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
   TE* X = reinterpret_cast<TE*>(g.X0) + tr.m * g.x_stride;
 
   const int t = threadIdx.x;
-  const int rb = t >> 4;          // 0..15
-  const int cq = (t & 15) * 4;    // 0..60
-  const bool vec = (sc0 + T <= g.cols) && ((g.cols & 3) == 0) && aligned16(M) &&
+  // 4 consecutive elements per thread; TC/4 threads per row, 4 sweeps
+  const int tpr = TC / 4;
+  const int rb = t / tpr;         // 0..15 (64x64) or 0..3 (16x256)
+  const int cq = (t % tpr) * 4;   // 0..60 or 0..252
+  const int rstep = 256 / tpr;
+  const bool vec = (sc0 + cq + 4 <= g.cols) && ((g.cols & 3) == 0) && aligned16(M) &&
                    ((reinterpret_cast<uintptr_t>(G) & (BF16 ? 7u : 15u)) == 0);
 
   float u[4][4];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int r = sr0 + rb + 16 * k;
+    const int r = sr0 + rb + rstep * k;
 #pragma unroll
     for (int e = 0; e < 4; ++e) u[k][e] = 0.f;
     if (r < g.rows) {
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
   if (!g.trans) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      Vec4<BF16>::store(X + int64_t(i0 + rb + 16 * k) * g.q_pad + j0 + cq, u[k]);
+      Vec4<BF16>::store(X + int64_t(i0 + rb + rstep * k) * g.q_pad + j0 + cq, u[k]);
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k)

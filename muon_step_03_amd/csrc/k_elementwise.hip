@@ -1,9 +1,10 @@
 // Elementwise phases of the Muon step: the head (momentum, Nesterov
 // look-ahead, Frobenius-norm partials, X0 write in short-side orientation)
 // and the tail (MuonGS reductions, projection, RMS scale, decoupled weight
-// decay, W update).  Both are HBM-bound; each block moves one 64x64 tile with
-// coalesced accesses, transposing through LDS when a tall matrix is iterated
-// as its transpose.
+// decay, W update).  Both are HBM-bound; each block moves one tile of 4096
+// elements with coalesced accesses (16x256 for a wide matrix, 64x64
+// transposed through LDS for a tall one, which is iterated as its
+// transpose).
 //
 // Passages: update order — "[Deep Learning] Muon — 행렬 업데이트를 직교화하는
 // 옵티마이저", section 3; SGD-momentum/Nesterov defaults and the 1e-7
@@ -25,8 +26,7 @@ struct TileRef {
   int tile;      // tile index within the matrix
 };
 
-__device__ __forceinline__ TileRef decode(const Batch& bt, const Work& wk) {
-  const int64_t bid = blockIdx.x;
+__device__ __forceinline__ TileRef decode(const Batch& bt, const Work& wk, int64_t bid) {
   const int gi = find_group(wk, bid);
   const int64_t local = bid - wk.begin[gi];
   const int tiles = wk.tiles[gi];
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
   __shared__ float S[T][T + 1];
   __shared__ float red[4];
 
-  const TileRef tr = decode(bt, wk);
+  const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
   // A wide matrix (X = U, no transpose) is taken in tiles of 16 rows x 256
   // columns (row runs of 512 / 1024 bytes of G / M), a tall one in 64 x 64
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
 // summation order).
 __global__ __launch_bounds__(256) void norm_finalize_kernel(Batch bt, Work wk) {
   __shared__ float red[4];
-  const TileRef tr = decode(bt, wk);
+  const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
   const float* part = g.head_part + tr.m * g.head_tiles;
   float s = 0.f;
@@ -215,56 +215,91 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(Batch bt, Work wk) {
 }
 
 // ------------------------------------------------------------------- tail
-// Gathers, for the thread's 4x4 elements of a 64x64 weight tile at (r0, c0),
-// the Newton-Schulz output O in weight orientation (through LDS when the
-// iterate is the transpose).  Every X access lies inside the padded extents.
-template <bool BF16>
-__device__ __forceinline__ void load_o_tile(const MatGroup& g, const typename Elem<BF16>::T* X,
-                                            int r0, int c0, float (*S)[T + 1], float o[4][4]) {
+// A tail tile is 64x64 in weight orientation, or, for a wide matrix whose
+// rows are a multiple of 64 and columns a multiple of 256 (and no row/column
+// statistics wanted), 16 rows x 256 columns: row runs of 512 bytes of W and
+// O, and the same tile count.  Each thread holds 4 consecutive columns of 4
+// rows, rstep rows apart.
+struct TailTile {
+  int r0, c0;   // weight-orientation origin
+  int rb, cq;   // thread's first row offset and column offset
+  int rstep;    // row distance between the thread's 4 rows
+  int tc;       // tile columns (64 or 256)
+};
+
+__device__ __forceinline__ TailTile tail_tile(const MatGroup& g, int tile, bool allow_flat) {
   const int t = threadIdx.x;
-  const int rb = t >> 4, cq = (t & 15) * 4;
+  TailTile tt;
+  if (allow_flat && !g.trans && (g.rows % T) == 0 && (g.cols % (4 * T)) == 0) {
+    const int ntc = g.cols / (4 * T);
+    const int ti = tile / ntc;
+    tt.r0 = ti * (T / 4);
+    tt.c0 = (tile - ti * ntc) * (4 * T);
+    tt.rb = t >> 6;
+    tt.cq = (t & 63) * 4;
+    tt.rstep = 4;
+    tt.tc = 4 * T;
+  } else {
+    const int ti = tile / g.tail_tiles_c;
+    tt.r0 = ti * T;
+    tt.c0 = (tile - ti * g.tail_tiles_c) * T;
+    tt.rb = t >> 4;
+    tt.cq = (t & 15) * 4;
+    tt.rstep = 16;
+    tt.tc = T;
+  }
+  return tt;
+}
+
+// Gathers the thread's 4x4 elements of the Newton-Schulz output O in weight
+// orientation (through LDS when the iterate is the transpose; such tiles are
+// always 64x64).  Every X access lies inside the padded extents.
+template <bool BF16, bool NT>
+__device__ __forceinline__ void load_o_tile(const MatGroup& g, const typename Elem<BF16>::T* X,
+                                            const TailTile& tt, float (*S)[T + 1], float o[4][4]) {
   if (!g.trans) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      Vec4<BF16>::load(X + int64_t(r0 + rb + 16 * k) * g.q_pad + c0 + cq, o[k]);
+    for (int k = 0; k < 4; ++k) {
+      const auto* p = X + int64_t(tt.r0 + tt.rb + tt.rstep * k) * g.q_pad + tt.c0 + tt.cq;
+      if (NT) load4_nt(p, o[k]); else Vec4<BF16>::load(p, o[k]);
+    }
   } else {
     // X rows are weight columns: read X[c0 + i][r0 + j] coalesced, then
     // transpose through LDS.
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float v[4];
-      Vec4<BF16>::load(X + int64_t(c0 + rb + 16 * k) * g.q_pad + r0 + cq, v);
+      const auto* p = X + int64_t(tt.c0 + tt.rb + 16 * k) * g.q_pad + tt.r0 + tt.cq;
+      if (NT) load4_nt(p, v); else Vec4<BF16>::load(p, v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[rb + 16 * k][cq + e] = v[e];
+      for (int e = 0; e < 4; ++e) S[tt.rb + 16 * k][tt.cq + e] = v[e];
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[k][e] = S[cq + e][rb + 16 * k];
+      for (int e = 0; e < 4; ++e) o[k][e] = S[tt.cq + e][tt.rb + 16 * k];
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool NT>
 __device__ __forceinline__ void load_w_tile(const MatGroup& g, const typename Elem<BF16>::T* W,
-                                            int r0, int c0, float w[4][4], bool valid[4][4]) {
+                                            const TailTile& tt, float w[4][4], bool valid[4][4]) {
   using E = Elem<BF16>;
-  const int t = threadIdx.x;
-  const int rb = t >> 4, cq = (t & 15) * 4;
-  const bool vec = (c0 + T <= g.cols) && ((g.cols & 3) == 0) &&
+  const bool vec = (tt.c0 + tt.tc <= g.cols) && ((g.cols & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(W) & (BF16 ? 7u : 15u)) == 0);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int r = r0 + rb + 16 * k;
-    const int64_t off = int64_t(r) * g.cols + c0 + cq;
+    const int r = tt.r0 + tt.rb + tt.rstep * k;
+    const int64_t off = int64_t(r) * g.cols + tt.c0 + tt.cq;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       w[k][e] = 0.f;
-      valid[k][e] = (r < g.rows) && (c0 + cq + e < g.cols);
+      valid[k][e] = (r < g.rows) && (tt.c0 + tt.cq + e < g.cols);
     }
     if (r < g.rows) {
       if (vec) {
-        Vec4<BF16>::load(W + off, w[k]);
+        if (NT) load4_nt(W + off, w[k]); else Vec4<BF16>::load(W + off, w[k]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -274,18 +309,37 @@ __device__ __forceinline__ void load_w_tile(const MatGroup& g, const typename El
   }
 }
 
+// Block sums of three values with one pair of barriers.
+__device__ __forceinline__ void block_sum3_256(float& a, float& b, float& c, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
+    c += __shfl_xor(c, off, 64);
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red[wave] = a;
+    red[4 + wave] = b;
+    red[8 + wave] = c;
+  }
+  __syncthreads();
+  a = (red[0] + red[1]) + (red[2] + red[3]);
+  b = (red[4] + red[5]) + (red[6] + red[7]);
+  c = (red[8] + red[9]) + (red[10] + red[11]);
+}
+
 // Per-tile partials of <W,O>, ||W||^2, ||O||^2 (O scaled by 1/(||U||+eps)
 // when no Newton-Schulz step ran, since X0 holds the unnormalised U).
 template <bool BF16>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int ns_steps, int rc) {
   using TE = typename Elem<BF16>::T;
   __shared__ float S[T][T + 1];
-  __shared__ float red[4];
-  const TileRef tr = decode(bt, wk);
+  __shared__ float red[12];
+  const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
-  const int tr_ = tr.tile / g.tail_tiles_c;
-  const int tc_ = tr.tile - tr_ * g.tail_tiles_c;
-  const int r0 = tr_ * T, c0 = tc_ * T;
+  const TailTile tt = tail_tile(g, tr.tile, !rc);
   const int64_t elems = int64_t(g.rows) * g.cols;
   const TE* W = mat_cptr<TE>(reinterpret_cast<const void* const*>(g.W_tab), g.W, tr.m, elems);
   const TE* X = reinterpret_cast<const TE*>((ns_steps & 1) ? g.X1 : g.X0) + tr.m * g.x_stride;
@@ -293,8 +347,10 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
 
   float w[4][4], o[4][4];
   bool valid[4][4];
-  load_w_tile<BF16>(g, W, r0, c0, w, valid);
-  load_o_tile<BF16>(g, X, r0, c0, S, o);
+  // nontemporal: the reduction reads W and O at 5.2 instead of 4.3 TB/s
+  // (the apply, which reads them again, is no slower for it)
+  load_w_tile<BF16, true>(g, W, tt, w, valid);
+  load_o_tile<BF16, true>(g, X, tt, S, o);
   float dot = 0.f, ww = 0.f, oo = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -305,9 +361,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
       ww = fmaf(w[k][e], w[k][e], ww);
       oo = fmaf(ov, ov, oo);
     }
-  dot = block_sum_256(dot, red);
-  ww = block_sum_256(ww, red);
-  oo = block_sum_256(oo, red);
+  block_sum3_256(dot, ww, oo, red);
   if (threadIdx.x == 0) {
     float* p = g.tail_part + (tr.m * g.tail_tiles + tr.tile) * 3;
     p[0] = dot;
@@ -315,11 +369,11 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
     p[2] = oo;
   }
   if (rc) {
-    // Row and column sums of O^2 over this tile: 64 + 64 partials.  A row's
-    // 64 values sit in 16 consecutive threads (shuffle reduction); a
-    // column's in the 16 row groups (through LDS).
+    // Row and column sums of O^2 over this 64x64 tile: 64 + 64 partials.
+    // A row's 64 values sit in 16 consecutive threads (shuffle reduction);
+    // a column's in the 16 row groups (through LDS).
     const int t = threadIdx.x;
-    const int rb = t >> 4, cq = (t & 15) * 4;
+    const int rb = tt.rb, cq = tt.cq;
     float* out = g.rc_part + (tr.m * g.tail_tiles + tr.tile) * (2 * T);
     float rs[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -357,10 +411,11 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
 // from the tile partials, the direction to equalise (NorMuon: rows; MeqMuon:
 // the one whose norms have the larger std/mean, rows on a tie), and the
 // scales target/norm along it (target = ||O||_F / sqrt(count), 0 for a zero
-// row or column) and 1 along the other.
+// row or column) and 1 along the other.  The partial sums run in tile order;
+// the inner loops are unrolled so that their loads are in flight together.
 __global__ __launch_bounds__(256) void rc_finalize_kernel(Batch bt, Work wk, int variant) {
   __shared__ float red[4];
-  const TileRef tr = decode(bt, wk);
+  const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
   const int tcn = g.tail_tiles_c, trn = g.tail_tiles / g.tail_tiles_c;
   const float* part = g.rc_part + tr.m * g.tail_tiles * (2 * T);
@@ -369,16 +424,20 @@ __global__ __launch_bounds__(256) void rc_finalize_kernel(Batch bt, Work wk, int
   float sum_r = 0.f, sum_c = 0.f, s2 = 0.f;
   for (int r = threadIdx.x; r < g.rows; r += 256) {
     const int ti = r / T, ri = r - ti * T;
+    const float* pr = part + int64_t(ti) * tcn * (2 * T) + ri;
     float a = 0.f;
-    for (int tc = 0; tc < tcn; ++tc) a += part[(ti * tcn + tc) * (2 * T) + ri];
+#pragma unroll 8
+    for (int tc = 0; tc < tcn; ++tc) a += pr[tc * (2 * T)];
     srow[r] = a;
     sum_r += sqrtf(a);
     s2 += a;
   }
   for (int c = threadIdx.x; c < g.cols; c += 256) {
     const int tc = c / T, ci = c - tc * T;
+    const float* pc = part + int64_t(tc) * (2 * T) + T + ci;
     float a = 0.f;
-    for (int ti = 0; ti < trn; ++ti) a += part[(ti * tcn + tc) * (2 * T) + T + ci];
+#pragma unroll 8
+    for (int ti = 0; ti < trn; ++ti) a += pc[int64_t(ti) * tcn * (2 * T)];
     scol[c] = a;
     sum_c += sqrtf(a);
   }
@@ -422,8 +481,8 @@ __global__ __launch_bounds__(256) void rc_finalize_kernel(Batch bt, Work wk, int
 // Per-matrix totals: ||W||^2, <W,O>, ||O||^2, the MuonGS coefficient and the
 // optional stats.
 __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, int variant) {
-  __shared__ float red[4];
-  const TileRef tr = decode(bt, wk);
+  __shared__ float red[12];
+  const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
   const float* part = g.tail_part + tr.m * g.tail_tiles * 3;
   float dot = 0.f, ww = 0.f, oo = 0.f;
@@ -432,9 +491,7 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
     ww += part[3 * i + 1];
     oo += part[3 * i + 2];
   }
-  dot = block_sum_256(dot, red);
-  ww = block_sum_256(ww, red);
-  oo = block_sum_256(oo, red);
+  block_sum3_256(dot, ww, oo, red);
   if (threadIdx.x == 0) {
     const float coef = (variant == MUON_VARIANT_MUONGS && ww > 0.f) ? dot / ww : 0.f;
     float hscale = 1.f;
@@ -462,17 +519,18 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
 
 // W' = h * ((1 - lr*wd) W - lr*s*(O - coef*W)): coef the MuonGS projection
 // coefficient, h the MuonH renormalisation (coef = 0, h = 1 for plain Muon).
+// Blocks run in the reverse of the reduction's order, so that the first
+// ones find the W and O tiles that the reduction read last still in the
+// Infinity Cache.
 template <bool BF16>
 __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int ns_steps,
                                                          int reduced, int rc) {
   using E = Elem<BF16>;
   using TE = typename E::T;
   __shared__ float S[T][T + 1];
-  const TileRef tr = decode(bt, wk);
+  const TileRef tr = decode(bt, wk, reduced ? gridDim.x - 1 - blockIdx.x : blockIdx.x);
   const MatGroup& g = *tr.g;
-  const int tr_ = tr.tile / g.tail_tiles_c;
-  const int tc_ = tr.tile - tr_ * g.tail_tiles_c;
-  const int r0 = tr_ * T, c0 = tc_ * T;
+  const TailTile tt = tail_tile(g, tr.tile, !rc);
   const int64_t elems = int64_t(g.rows) * g.cols;
   TE* W = mat_ptr<TE>(g.W_tab, g.W, tr.m, elems);
   const TE* X = reinterpret_cast<const TE*>((ns_steps & 1) ? g.X1 : g.X0) + tr.m * g.x_stride;
@@ -486,31 +544,35 @@ __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int 
 
   float w[4][4], o[4][4];
   bool valid[4][4];
-  load_w_tile<BF16>(g, W, r0, c0, w, valid);
-  load_o_tile<BF16>(g, X, r0, c0, S, o);
+  load_w_tile<BF16, false>(g, W, tt, w, valid);
+  load_o_tile<BF16, false>(g, X, tt, S, o);
 
-  const int t = threadIdx.x;
-  const int rb = t >> 4, cq = (t & 15) * 4;
   if (rc) {
-    // NorMuon / MeqMuon: O scaled per row and per column (one of the two is 1)
+    // NorMuon / MeqMuon: O scaled per row and per column (one of the two is
+    // 1); indices clamped so that a ragged tile reads inside the matrix's
+    // scales (the clamped products are never stored).
     const float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
     const float* scol = srow + g.rows;
+    float rsc[4], csc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rsc[k] = srow[min(tt.r0 + tt.rb + tt.rstep * k, g.rows - 1)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) csc[e] = scol[min(tt.c0 + tt.cq + e, g.cols - 1)];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (valid[k][e]) o[k][e] *= srow[r0 + rb + 16 * k] * scol[c0 + cq + e];
+      for (int e = 0; e < 4; ++e) o[k][e] *= rsc[k] * csc[e];
   }
-  const bool vec = (c0 + T <= g.cols) && ((g.cols & 3) == 0) &&
+  const bool vec = (tt.c0 + tt.tc <= g.cols) && ((g.cols & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(W) & (BF16 ? 7u : 15u)) == 0);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int r = r0 + rb + 16 * k;
+    const int r = tt.r0 + tt.rb + tt.rstep * k;
     if (r >= g.rows) continue;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = fmaf(wcoef, w[k][e], -ocoef * o[k][e]);
-    const int64_t off = int64_t(r) * g.cols + c0 + cq;
+    const int64_t off = int64_t(r) * g.cols + tt.c0 + tt.cq;
     if (vec) {
       Vec4<BF16>::store(W + off, v);
     } else {

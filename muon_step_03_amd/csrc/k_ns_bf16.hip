@@ -93,6 +93,9 @@ struct Cfg;
 #define MUON_UPD_STAGES 3
 #endif
 // Wave grid of the update block: WGM rows of waves.
+#ifndef MUON_TAIL_GS
+#define MUON_TAIL_GS 4
+#endif
 #ifndef MUON_UPD_WGM
 #define MUON_UPD_WGM 2
 #endif
@@ -346,18 +349,23 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   const int64_t stepB = MODE == MODE_UPDATE ? int64_t(BK) * ldb * 2 : int64_t(BK) * 2;
 
   // Issue the loads of K step `kt` into stage buffer J (= kt % S).  Each wave
-  // moves A_INSTR + B_INSTR KiB-sized pieces.
-  auto issue = [&](auto bufc, int kt) {
+  // moves A_INSTR + B_INSTR KiB-sized pieces.  A diagonal tile of a
+  // symmetric product (D: both operands are the same rows) loads only A and
+  // reads its B fragments from the A buffers.
+  auto issue = [&](auto bufc, auto diagc, int kt) {
     constexpr int J = decltype(bufc)::value;
+    constexpr bool D = decltype(diagc)::value;
     const char* a = gA + kt * stepA;
     const char* b = gB + kt * stepB;
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i)
       dma16(offA[i], a, smem_base + uint32_t(J * A_BYTES + (wave * A_INSTR + i) * WAVE_BYTES));
+    if constexpr (!D) {
 #pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-      dma16(offB[i], b,
-            smem_base + uint32_t(S * A_BYTES + J * B_BYTES + (wave * B_INSTR + i) * WAVE_BYTES));
+      for (int i = 0; i < B_INSTR; ++i)
+        dma16(offB[i], b,
+              smem_base + uint32_t(S * A_BYTES + J * B_BYTES + (wave * B_INSTR + i) * WAVE_BYTES));
+    }
   };
 
   f32x16_t acc[WM][WN];
@@ -369,10 +377,10 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
   // Fragments of one 16-deep K sub-step of stage buffer J.
-  auto load_frags = [&](auto bufc, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
+  auto load_frags = [&](auto bufc, auto diagc, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
     constexpr int J = decltype(bufc)::value;
     const LDS_AS char* sA = smem + J * A_BYTES;
-    const LDS_AS char* sB = smem + S * A_BYTES + J * B_BYTES;
+    const LDS_AS char* sB = decltype(diagc)::value ? sA : smem + S * A_BYTES + J * B_BYTES;
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi)
@@ -399,14 +407,15 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // Waits until the loads of `stage` are done, given that the last stage
   // issued so far is `issued` (capped at nk-1): exactly the loads of the
   // stages issued after `stage` may stay in flight (vmcnt counts in order).
-  auto wait_stage = [&](int stage, int issued) {
+  auto wait_stage = [&](auto diagc, int stage, int issued) {
+    constexpr int L = decltype(diagc)::value ? A_INSTR : LOADS;  // loads per stage
     const int younger = (issued < nk - 1 ? issued : nk - 1) - stage;
     if (S > 3 && younger >= 3)
-      wait_vmcnt<(S > 3 ? 3 : 0) * LOADS>();
+      wait_vmcnt<(S > 3 ? 3 : 0) * L>();
     else if (younger == 2)
-      wait_vmcnt<2 * LOADS>();
+      wait_vmcnt<2 * L>();
     else if (younger == 1)
-      wait_vmcnt<LOADS>();
+      wait_vmcnt<L>();
     else
       wait_vmcnt<0>();
   };
@@ -420,6 +429,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // every wave) becomes readable.  The loop is unrolled by S so that every
   // stage buffer index is a compile-time constant.
   bf16x8_t a0[WM], b0[WN], a1[WM], b1[WN];
+  auto kloop = [&](auto dg) {
   if constexpr (C::NW == 8 && KS == 2) {
   // Eight waves, two per SIMD: the waves 0-3 and 4-7 run half a K step
   // apart, so that on every SIMD one wave issues its MFMAs while the other
@@ -433,23 +443,23 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // barrier after which the first group reads it: each wave waits for its
   // own loads of it at the end of its phase before that barrier.
   const bool late = wave >= 4;
-  issue(std::integral_constant<int, 0>{}, 0);
-  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
-  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, 2);
-  wait_stage(0, S - 2);  // the prologue issued steps 0 .. S-2
+  issue(std::integral_constant<int, 0>{}, dg, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, dg, 1);
+  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, dg, 2);
+  wait_stage(dg, 0, S - 2);  // the prologue issued steps 0 .. S-2
   block_barrier();
   if (late) block_barrier();
   static_assert(KS == 2, "the ping-pong loop holds the fragments of one 32-deep K step");
   auto pp = [&](auto bufc, int kt) {
     constexpr int J = decltype(bufc)::value;
-    load_frags(bufc, 0, a0, b0);
-    load_frags(bufc, 1, a1, b1);
-    if (kt + S - 1 < nk) issue(std::integral_constant<int, (J + S - 1) % S>{}, kt + S - 1);
-    if (late && kt + 1 < nk) wait_stage(kt + 1, kt + S - 1);
+    load_frags(bufc, dg, 0, a0, b0);
+    load_frags(bufc, dg, 1, a1, b1);
+    if (kt + S - 1 < nk) issue(std::integral_constant<int, (J + S - 1) % S>{}, dg, kt + S - 1);
+    if (late && kt + 1 < nk) wait_stage(dg, kt + 1, kt + S - 1);
     block_barrier();
     mfmas(a0, b0);
     mfmas(a1, b1);
-    if (!late && kt + 1 < nk) wait_stage(kt + 1, kt + S - 1);
+    if (!late && kt + 1 < nk) wait_stage(dg, kt + 1, kt + S - 1);
     block_barrier();
   };
   for (int kt = 0; kt < nk; kt += S) {
@@ -460,28 +470,28 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   }
   if (!late) block_barrier();
   } else {
-  issue(std::integral_constant<int, 0>{}, 0);
-  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
-  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, 2);
-  if constexpr (S > 3) if (3 < nk) issue(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, 3);
-  wait_stage(0, S - 1);  // the prologue issued steps 0 .. S-1
+  issue(std::integral_constant<int, 0>{}, dg, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, dg, 1);
+  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, dg, 2);
+  if constexpr (S > 3) if (3 < nk) issue(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, dg, 3);
+  wait_stage(dg, 0, S - 1);  // the prologue issued steps 0 .. S-1
   block_barrier();
-  load_frags(std::integral_constant<int, 0>{}, 0, a0, b0);
+  load_frags(std::integral_constant<int, 0>{}, dg, 0, a0, b0);
   auto step = [&](auto bufc, int kt) {
     constexpr int J = decltype(bufc)::value;
-    load_frags(bufc, 1, a1, b1);
+    load_frags(bufc, dg, 1, a1, b1);
     mfmas(a0, b0);
     if constexpr (KS == 4) {
-      load_frags(bufc, 2, a0, b0);
+      load_frags(bufc, dg, 2, a0, b0);
       mfmas(a1, b1);
-      load_frags(bufc, 3, a1, b1);
+      load_frags(bufc, dg, 3, a1, b1);
       mfmas(a0, b0);
     }
     if (kt + 1 < nk) {
-      wait_stage(kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
+      wait_stage(dg, kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
       block_barrier();
-      if (kt + S < nk) issue(bufc, kt + S);
-      load_frags(std::integral_constant<int, (J + 1) % S>{}, 0, a0, b0);
+      if (kt + S < nk) issue(bufc, dg, kt + S);
+      load_frags(std::integral_constant<int, (J + 1) % S>{}, dg, 0, a0, b0);
     }
     mfmas(a1, b1);
   };
@@ -491,6 +501,15 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     if constexpr (S > 2) if (kt + 2 < nk) step(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, kt + 2);
     if constexpr (S > 3) if (kt + 3 < nk) step(std::integral_constant<int, (S > 3 ? 3 : 0)>{}, kt + 3);
   }
+  }
+  };
+  if constexpr (MODE != MODE_UPDATE) {
+    if (ti == tj)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
+  } else {
+    kloop(std::false_type{});
   }
 
   // ---- Epilogue: the final fp32 tile is staged through LDS in two passes
@@ -718,88 +737,91 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     uint16_t* Wm = mat_ptr<uint16_t>(g.W_tab, g.W, m, int64_t(g.rows) * g.cols);
     const int64_t wld = g.cols;
     const bool wvec = (reinterpret_cast<uintptr_t>(Wm) & 15) == 0;
-    // The 8-wave tiles load all 16-byte W chunks of the pass before the
-    // first W' store (which the compiler may not move loads across) so that
-    // their latencies overlap: by rows for a wide W, by columns for a tall
-    // one.  The 4-wave update has no registers to spare for them.
-    constexpr bool kPreW = C::NW == 8;
-    uint4 lin[CHUNKS], wv[kPreW ? CHUNKS : 1];
+    // All 16-byte W chunks of a group are loaded before the group's first W'
+    // store (which the compiler may not move loads across), so that their
+    // latencies overlap: by rows for a wide W, by columns for a tall one.
+    // The 8-wave tiles take the pass in one group; the 4-wave update, which
+    // has fewer registers to spare, in groups of GS chunks.
+    constexpr int GS = (C::NW == 8 || CHUNKS < MUON_TAIL_GS) ? CHUNKS : MUON_TAIL_GS;
+    static_assert(CHUNKS % GS == 0, "chunk groups");
 #pragma unroll
-    for (int u = 0; u < CHUNKS; ++u) {
-      const int q = t + NT * u;
-      const int row = q / CPR, col = (q % CPR) * 8;
-      lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
-      if constexpr (kPreW) {
+    for (int u0 = 0; u0 < CHUNKS; u0 += GS) {
+      uint4 lin[GS], wv[GS];
+#pragma unroll
+      for (int u = 0; u < GS; ++u) {
+        const int q = t + NT * (u0 + u);
+        const int row = q / CPR, col = (q % CPR) * 8;
+        lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
         const int i = i0 + 64 * pass + row, j = j0 + col;
         wv[u] = make_uint4(0, 0, 0, 0);
         if (!g.trans && wvec && i < g.p && j < g.q)
           wv[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(i) * wld + j);
       }
-    }
 #pragma unroll
-    for (int u = 0; u < CHUNKS; ++u) {
-      const int q = t + NT * u;
-      const int row = q / CPR, col = (q % CPR) * 8;
-      float v[8];
-      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
-      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
+      for (int u = 0; u < GS; ++u) {
+        const int q = t + NT * (u0 + u);
+        const int row = q / CPR, col = (q % CPR) * 8;
+        float v[8];
+        const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
+        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = v0[e];
-        v[e + 4] = v1[e];
-      }
-      add_lin(v, lin[u]);
-      const int i = i0 + 64 * pass + row, j = j0 + col;
-      if (!g.trans) {
-        if (i < g.p && j < g.q) {
-          uint16_t* wp = Wm + int64_t(i) * wld + j;
-          if constexpr (kPreW) {
+        for (int e = 0; e < 4; ++e) {
+          v[e] = v0[e];
+          v[e + 4] = v1[e];
+        }
+        add_lin(v, lin[u]);
+        const int i = i0 + 64 * pass + row, j = j0 + col;
+        if (!g.trans) {
+          if (i < g.p && j < g.q) {
+            uint16_t* wp = Wm + int64_t(i) * wld + j;
             if (wvec)
               *reinterpret_cast<uint4*>(wp) = w_apply(wv[u], v);
             else
               w_update(wp, false, v);
-          } else {
-            w_update(wp, wvec, v);
           }
+        } else {
+          // O is needed by columns: keep the complete values in T
+          *(LDS_AS f32x4_t*)(T + row * TP + col) = f32x4_t{v[0], v[1], v[2], v[3]};
+          *(LDS_AS f32x4_t*)(T + row * TP + col + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
         }
-      } else {
-        // O is needed by columns: keep the complete values in T
-        *(LDS_AS f32x4_t*)(T + row * TP + col) = f32x4_t{v[0], v[1], v[2], v[3]};
-        *(LDS_AS f32x4_t*)(T + row * TP + col + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
       }
     }
     if (g.trans) {
       constexpr int MC = BN * 8 / NT;
-      // W row j0 + c, columns i0 + 64 pass + r8 .. +7, from staged column c
-      uint4 wt[kPreW ? MC : 1];
-      if constexpr (kPreW) {
+      constexpr int MGS = (C::NW == 8 || MC < MUON_TAIL_GS) ? MC : MUON_TAIL_GS;
+      static_assert(MC % MGS == 0, "mirrored chunk groups");
+      // W row j0 + c, columns i0 + 64 pass + r8 .. +7, from staged column c;
+      // the first group's W loads are issued before the barrier.
+      uint4 wt[MGS];
+      auto load_wt = [&](int u0) {
 #pragma unroll
-        for (int u = 0; u < MC; ++u) {
-          const int q = t + NT * u;
+        for (int u = 0; u < MGS; ++u) {
+          const int q = t + NT * (u0 + u);
           const int c = q % BN, r8 = (q / BN) * 8;
           const int i = i0 + 64 * pass + r8, j = j0 + c;
           wt[u] = make_uint4(0, 0, 0, 0);
           if (wvec && j < g.q && i < g.p) wt[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(j) * wld + i);
         }
-      }
+      };
+      load_wt(0);
       block_barrier();
 #pragma unroll
-      for (int u = 0; u < MC; ++u) {
-        const int q = t + NT * u;
-        const int c = q % BN, r8 = (q / BN) * 8;  // consecutive lanes: distinct banks
-        const int i = i0 + 64 * pass + r8, j = j0 + c;
-        if (j >= g.q || i >= g.p) continue;
-        float v[8];
+      for (int u0 = 0; u0 < MC; u0 += MGS) {
+        if (u0 > 0) load_wt(u0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
-        uint16_t* wp = Wm + int64_t(j) * wld + i;
-        if constexpr (kPreW) {
+        for (int u = 0; u < MGS; ++u) {
+          const int q = t + NT * (u0 + u);
+          const int c = q % BN, r8 = (q / BN) * 8;  // consecutive lanes: distinct banks
+          const int i = i0 + 64 * pass + r8, j = j0 + c;
+          if (j >= g.q || i >= g.p) continue;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
+          uint16_t* wp = Wm + int64_t(j) * wld + i;
           if (wvec)
             *reinterpret_cast<uint4*>(wp) = w_apply(wt[u], v);
           else
             w_update(wp, false, v);
-        } else {
-          w_update(wp, wvec, v);
         }
       }
     }

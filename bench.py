@@ -8,7 +8,9 @@ momentum/Nesterov head, 5 Newton-Schulz iterations, scale/decay/update tail,
 issued as ONE grouped launch sequence (muon_step_grouped) on inputs already
 resident in HBM (the 2k-hidden stress set, whose whole-model workspace would
 not fit beside its 189 GB of W, G and M, as a few calls over even chunks of
-its groups, --max-workspace-gb).  Prints one JSON line:
+its groups, --max-workspace-gb).  Without --warmup, the untimed warmup runs
+as many steps as take 0.25 s (at least 3): on the GPU the first ten or so
+steps run up to 20 % slower while its clocks ramp up.  Prints one JSON line:
 
   value       optimizer steps per second (whole job = one GPU)
   roofline    the dominant kernel (the Newton-Schulz update GEMM): its
@@ -43,7 +45,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: as many as take 0.25 s, at least 3: "
+                         "the GPU's clocks ramp up over the first tens of milliseconds)")
     ap.add_argument("--workload", default="gpt160m")
     ap.add_argument("--variant", default="muon", choices=["muon", "muongs", "muonh", "normuon", "meqmuon"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -190,7 +194,7 @@ def aux_adamw(args, wl, dev, stream, muon_ms):
         state["t"] += 1
         adamw_step_grouped(descs, torch.bfloat16, step=state["t"], stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(args.warmup or 3):
         call()
     torch.cuda.synchronize()
     L = _lib.lib()
@@ -256,8 +260,19 @@ def main():
         for groups in calls:
             muon_step_grouped(groups, tdtype, workspace=ws, device=dev, stream=stream, **hp)
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        # by time: at least 3 steps and 0.25 s of work
+        torch.cuda.synchronize()
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 3 or time.perf_counter() - t_w < 0.25:
+            step()
+            n_w += 1
+            if n_w % 8 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n_w
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 

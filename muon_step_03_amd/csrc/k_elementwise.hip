@@ -23,7 +23,8 @@ constexpr int T = kEwTile;  // 64
 struct TileRef {
   const MatGroup* g;
   int64_t m;     // matrix index within the group
-  int tile;      // tile index within the matrix
+  int tile;      // tile (block) index within the matrix
+  int per;       // tiles (blocks) per matrix in this launch
 };
 
 __device__ __forceinline__ TileRef decode(const Batch& bt, const Work& wk, int64_t bid) {
@@ -34,6 +35,7 @@ __device__ __forceinline__ TileRef decode(const Batch& bt, const Work& wk, int64
   r.g = &bt.g[gi];
   r.m = local / tiles;
   r.tile = int(local - r.m * tiles);
+  r.per = tiles;
   return r;
 }
 
@@ -407,75 +409,96 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
   }
 }
 
-// NorMuon / MeqMuon, one block per matrix: squared row and column norms of O
-// from the tile partials, the direction to equalise (NorMuon: rows; MeqMuon:
-// the one whose norms have the larger std/mean, rows on a tie), and the
-// scales target/norm along it (target = ||O||_F / sqrt(count), 0 for a zero
-// row or column) and 1 along the other.  The partial sums run in tile order;
-// the inner loops are unrolled so that their loads are in flight together.
-__global__ __launch_bounds__(256) void rc_finalize_kernel(Batch bt, Work wk, int variant) {
-  __shared__ float red[4];
+// NorMuon / MeqMuon, first step: one block per chunk of kRcChunk rows (or
+// columns) of one matrix.  Each thread sums its row's (column's) squared
+// norm of O over the tile partials (tile order; unrolled by 8 so that the
+// loads are in flight together) and stores it; the block stores the
+// chunk's count, mean norm, sum of squared deviations from that mean, sum
+// of squared norms and count of non-zero norms.
+__global__ __launch_bounds__(256) void rc_sum_kernel(Batch bt, Work wk) {
+  __shared__ float red[12];
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
+  const int ncr = (g.rows + kRcChunk - 1) / kRcChunk;
+  const bool is_row = tr.tile < ncr;
+  const int chunk = is_row ? tr.tile : tr.tile - ncr;
+  const int n = is_row ? g.rows : g.cols;
+  const int idx = chunk * kRcChunk + int(threadIdx.x);
+  const bool valid = idx < n;
   const int tcn = g.tail_tiles_c, trn = g.tail_tiles / g.tail_tiles_c;
   const float* part = g.rc_part + tr.m * g.tail_tiles * (2 * T);
   float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
   float* scol = srow + g.rows;
-  float sum_r = 0.f, sum_c = 0.f, s2 = 0.f;
-  for (int r = threadIdx.x; r < g.rows; r += 256) {
-    const int ti = r / T, ri = r - ti * T;
-    const float* pr = part + int64_t(ti) * tcn * (2 * T) + ri;
-    float a = 0.f;
+  float a = 0.f;
+  if (valid) {
+    if (is_row) {
+      const int ti = idx / T, ri = idx - ti * T;
+      const float* pr = part + int64_t(ti) * tcn * (2 * T) + ri;
 #pragma unroll 8
-    for (int tc = 0; tc < tcn; ++tc) a += pr[tc * (2 * T)];
-    srow[r] = a;
-    sum_r += sqrtf(a);
-    s2 += a;
-  }
-  for (int c = threadIdx.x; c < g.cols; c += 256) {
-    const int tc = c / T, ci = c - tc * T;
-    const float* pc = part + int64_t(tc) * (2 * T) + T + ci;
-    float a = 0.f;
+      for (int tc = 0; tc < tcn; ++tc) a += pr[tc * (2 * T)];
+      srow[idx] = a;
+    } else {
+      const int tc = idx / T, ci = idx - tc * T;
+      const float* pc = part + int64_t(tc) * (2 * T) + T + ci;
 #pragma unroll 8
-    for (int ti = 0; ti < trn; ++ti) a += pc[int64_t(ti) * tcn * (2 * T)];
-    scol[c] = a;
-    sum_c += sqrtf(a);
+      for (int ti = 0; ti < trn; ++ti) a += pc[int64_t(ti) * tcn * (2 * T)];
+      scol[idx] = a;
+    }
   }
-  sum_r = block_sum_256(sum_r, red);
-  sum_c = block_sum_256(sum_c, red);
-  s2 = block_sum_256(s2, red);
-  // std/mean of the norms from a second pass over (norm - mean)^2 (the
-  // one-pass E[x^2]/E[x]^2 - 1 cancels badly for nearly equal norms)
-  const float mean_r = sum_r / float(g.rows), mean_c = sum_c / float(g.cols);
-  float dev_r = 0.f, dev_c = 0.f;
-  for (int r = threadIdx.x; r < g.rows; r += 256) {
-    const float d = sqrtf(srow[r]) - mean_r;
-    dev_r = fmaf(d, d, dev_r);
+  const int cnt = min(kRcChunk, n - chunk * kRcChunk);
+  const float nrm = valid ? sqrtf(a) : 0.f;
+  float sn = nrm, sa = a, nz = (valid && a > 0.f) ? 1.f : 0.f;
+  block_sum3_256(sn, sa, nz, red);
+  const float mean = sn / float(cnt);
+  const float dv = valid ? nrm - mean : 0.f;
+  const float m2 = block_sum_256(dv * dv, red);
+  if (threadIdx.x == 0) {
+    float* st = g.rc_stat + (tr.m * tr.per + tr.tile) * 5;
+    st[0] = float(cnt);
+    st[1] = mean;
+    st[2] = m2;
+    st[3] = sa;
+    st[4] = nz;
   }
-  for (int c = threadIdx.x; c < g.cols; c += 256) {
-    const float d = sqrtf(scol[c]) - mean_c;
-    dev_c = fmaf(d, d, dev_c);
+}
+
+// Second step, one block per matrix (one thread merges): the chunk
+// statistics of the rows and of the columns merged in chunk order (count,
+// mean and sum of squared deviations by the pairwise update of Chan et
+// al.), the direction to equalise (NorMuon: rows; MeqMuon: the one whose
+// norms have the larger std/mean, rows on a tie) and the common norm
+// target = ||O||_F / sqrt(count along it).  The apply kernel scales O by
+// target/norm along that direction (0 for a zero row or column).
+__global__ __launch_bounds__(64) void rc_finalize_kernel(Batch bt, Work wk, int variant) {
+  if (threadIdx.x != 0) return;
+  const TileRef tr = decode(bt, wk, blockIdx.x);
+  const MatGroup& g = *tr.g;
+  const int ncr = (g.rows + kRcChunk - 1) / kRcChunk;
+  const int nch = rc_chunks(g.rows, g.cols);
+  const float* st = g.rc_stat + tr.m * nch * 5;
+  float spread[2], sum_a[2], nz[2];
+  for (int side = 0; side < 2; ++side) {
+    const int c0 = side == 0 ? 0 : ncr, c1 = side == 0 ? ncr : nch;
+    float n = 0.f, mean = 0.f, m2 = 0.f, sa = 0.f, z = 0.f;
+    for (int c = c0; c < c1; ++c) {
+      const float* q = st + c * 5;
+      const float nb = q[0], nab = n + nb, delta = q[1] - mean;
+      mean = mean + delta * (nb / nab);
+      m2 = m2 + q[2] + delta * delta * (n * nb / nab);
+      n = nab;
+      sa += q[3];
+      z += q[4];
+    }
+    spread[side] = mean > 0.f ? sqrtf(m2 / n) / mean : 0.f;
+    sum_a[side] = sa;
+    nz[side] = z;
   }
-  dev_r = block_sum_256(dev_r, red);
-  dev_c = block_sum_256(dev_c, red);
-  const float spread_r = mean_r > 0.f ? sqrtf(dev_r / float(g.rows)) / mean_r : 0.f;
-  const float spread_c = mean_c > 0.f ? sqrtf(dev_c / float(g.cols)) / mean_c : 0.f;
-  const bool rows_dir = variant == MUON_VARIANT_NORMUON || spread_r >= spread_c;
-  const int n = rows_dir ? g.rows : g.cols;
-  const float target = sqrtf(s2 / float(n));
-  float nnz = 0.f;
-  for (int r = threadIdx.x; r < g.rows; r += 256) {
-    const float a = srow[r];
-    if (rows_dir && a > 0.f) nnz += 1.f;
-    srow[r] = rows_dir ? (a > 0.f ? target / sqrtf(a) : 0.f) : 1.f;
-  }
-  for (int c = threadIdx.x; c < g.cols; c += 256) {
-    const float a = scol[c];
-    if (!rows_dir && a > 0.f) nnz += 1.f;
-    scol[c] = rows_dir ? 1.f : (a > 0.f ? target / sqrtf(a) : 0.f);
-  }
-  nnz = block_sum_256(nnz, red);
-  if (threadIdx.x == 0 && g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 4] = target * target * nnz;
+  const bool rows_dir = variant == MUON_VARIANT_NORMUON || spread[0] >= spread[1];
+  const float target = sqrtf(sum_a[0] / float(rows_dir ? g.rows : g.cols));
+  float* sc = g.scal + tr.m * kScal;
+  sc[SC_RC_TARGET] = target;
+  sc[SC_RC_ROWS] = rows_dir ? 1.f : 0.f;
+  if (g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 4] = target * target * nz[rows_dir ? 0 : 1];
 }
 
 // Per-matrix totals: ||W||^2, <W,O>, ||O||^2, the MuonGS coefficient and the
@@ -548,16 +571,27 @@ __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int 
   load_o_tile<BF16, false>(g, X, tt, S, o);
 
   if (rc) {
-    // NorMuon / MeqMuon: O scaled per row and per column (one of the two is
-    // 1); indices clamped so that a ragged tile reads inside the matrix's
-    // scales (the clamped products are never stored).
+    // NorMuon / MeqMuon: O scaled by target/norm along the equalised
+    // direction (0 for a zero row or column), by 1 along the other; indices
+    // clamped so that a ragged tile reads inside the matrix's norms (the
+    // clamped products are never stored).
     const float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
     const float* scol = srow + g.rows;
+    // (both sets of norms loaded unconditionally, beside the two scalars,
+    // so that no load waits for another)
+    float ra[4], ca[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ra[k] = srow[min(tt.r0 + tt.rb + tt.rstep * k, g.rows - 1)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ca[e] = scol[min(tt.c0 + tt.cq + e, g.cols - 1)];
+    const float target = sc[SC_RC_TARGET];
+    const bool rows_dir = sc[SC_RC_ROWS] != 0.f;
+    auto scale_of = [&](float a) { return a > 0.f ? target / sqrtf(a) : 0.f; };
     float rsc[4], csc[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) rsc[k] = srow[min(tt.r0 + tt.rb + tt.rstep * k, g.rows - 1)];
+    for (int k = 0; k < 4; ++k) rsc[k] = rows_dir ? scale_of(ra[k]) : 1.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) csc[e] = scol[min(tt.c0 + tt.cq + e, g.cols - 1)];
+    for (int e = 0; e < 4; ++e) csc[e] = rows_dir ? 1.f : scale_of(ca[e]);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -614,8 +648,13 @@ hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hi
   return hipGetLastError();
 }
 
+hipError_t launch_rc_sum(const Batch& bt, const Work& wk, hipStream_t s) {
+  hipLaunchKernelGGL(rc_sum_kernel, grid_of(wk), dim3(256), 0, s, bt, wk);
+  return hipGetLastError();
+}
+
 hipError_t launch_rc_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s) {
-  hipLaunchKernelGGL(rc_finalize_kernel, grid_of(wk), dim3(256), 0, s, bt, wk, variant);
+  hipLaunchKernelGGL(rc_finalize_kernel, grid_of(wk), dim3(64), 0, s, bt, wk, variant);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ struct Layout {
   int64_t tile;             // NS GEMM block tile edge along p
   int64_t tile_n;           // update GEMM block tile edge along q
   size_t x_bytes, a_bytes, head_bytes, tail_bytes, scal_bytes;
-  size_t rc_bytes, rcs_bytes;  // row/column partials and scales (NorMuon, MeqMuon)
+  size_t rc_bytes, rcs_bytes, rcst_bytes;  // row/column partials, norms, chunk statistics
   size_t total;             // 0 on overflow
 };
 
@@ -78,9 +78,10 @@ Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
       !mul_ok(c, size_t(L.head_tiles) * 4, &h) || !mul_ok(c, size_t(L.tail_tiles) * 12, &t) ||
       !mul_ok(c, size_t(kScal) * 4, &s))
     return L;  // total stays 0
-  size_t rc, rcs;
+  size_t rc, rcs, rcst;
   if (!mul_ok(c, size_t(L.tail_tiles) * 2 * kEwTile * 4, &rc) ||
-      !mul_ok(c, size_t(rows + cols) * 4, &rcs))
+      !mul_ok(c, size_t(rows + cols) * 4, &rcs) ||
+      !mul_ok(c, size_t(rc_chunks(int(rows), int(cols))) * 5 * 4, &rcst))
     return L;
   L.x_bytes = align_up(x);
   L.a_bytes = align_up(a);
@@ -89,8 +90,9 @@ Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
   L.scal_bytes = align_up(s);
   L.rc_bytes = align_up(rc);
   L.rcs_bytes = align_up(rcs);
+  L.rcst_bytes = align_up(rcst);
   L.total = 2 * L.x_bytes + 2 * L.a_bytes + L.head_bytes + L.tail_bytes + L.scal_bytes +
-            L.rc_bytes + L.rcs_bytes;
+            L.rc_bytes + L.rcs_bytes + L.rcst_bytes;
   if (L.total < L.x_bytes) L.total = 0;
   return L;
 }
@@ -384,6 +386,8 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       base += L.rc_bytes;
       m.rc_scale = reinterpret_cast<float*>(base);
       base += L.rcs_bytes;
+      m.rc_stat = reinterpret_cast<float*>(base);
+      base += L.rcst_bytes;
       m.stats = stats ? stats + sel[k].stats_index * MUON_STATS_PER_MATRIX : nullptr;
       m.decay = float(1.0 - lr * wd);
       // Shape factor: Moonlight 0.2*sqrt(max(rows, cols)), or Keller
@@ -491,8 +495,18 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       const bool rc = h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON;
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, rc, s), 5, s, t0))) return st;
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, s), 6, s, t0))) return st;
-      if (rc && ((t0 = prof_start(s)), (st = finish_launch(launch_rc_finalize(bt, w_one, h.variant, s), 6, s, t0))))
-        return st;
+      if (rc) {
+        Work w_rc{};
+        w_rc.ngroups = nsel;
+        w_rc.begin[0] = 0;
+        for (int k = 0; k < nsel; ++k) {
+          w_rc.tiles[k] = rc_chunks(bt.g[k].rows, bt.g[k].cols);
+          w_rc.begin[k + 1] = w_rc.begin[k] + bt.g[k].count * w_rc.tiles[k];
+        }
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_rc_sum(bt, w_rc, s), 6, s, t0))) return st;
+        if ((t0 = prof_start(s)), (st = finish_launch(launch_rc_finalize(bt, w_one, h.variant, s), 6, s, t0)))
+          return st;
+      }
     }
     if (w_tail.begin[nsel] > 0 &&  // every group may have been finished by its last update
         ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),

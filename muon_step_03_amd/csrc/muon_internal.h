@@ -15,7 +15,8 @@
 //   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
 //   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
 //   rc      [count][tail_tiles][128] per-tile row and column sums of O^2
-//   rcs     [count][rows + cols]    row and column scales of O (NorMuon, MeqMuon)
+//   rcs     [count][rows + cols]    squared row and column norms of O (NorMuon, MeqMuon)
+//   rcst    [count][rc_chunks][5]   per-chunk statistics of those norms
 // Element type of X, A, B is bf16 (bit pattern in uint16_t) on the bf16 path
 // and float on the fp32 path.
 #pragma once
@@ -28,7 +29,12 @@
 namespace muon {
 
 constexpr int kMaxGroups = MUON_GROUPS_PER_LAUNCH;
-constexpr int kEwTile = 64;        // head/tail tile edge (elements)
+constexpr int kEwTile = 64;
+// Rows or columns per block of the NorMuon/MeqMuon norm sums.
+constexpr int kRcChunk = 256;
+inline __host__ __device__ int rc_chunks(int rows, int cols) {
+  return (rows + kRcChunk - 1) / kRcChunk + (cols + kRcChunk - 1) / kRcChunk;
+}        // head/tail tile edge (elements)
 // bf16 Newton-Schulz block tiles (wave tile = block tile / 2 in each
 // dimension, 4 waves per block).
 #ifndef MUON_SYRK_TILE
@@ -89,7 +95,9 @@ enum : int {
   SC_O2 = 4,     // ||O||_F^2
   SC_COEF = 5,   // MuonGS projection coefficient <W,O>/||W||^2 (0 otherwise)
   SC_HSCALE = 6, // MuonH renormalisation ||W|| / ||W^|| (1 otherwise)
-  kScal = 8
+  SC_RC_TARGET = 7,  // NorMuon/MeqMuon: the common norm ||O||_F / sqrt(count)
+  SC_RC_ROWS = 8,    // NorMuon/MeqMuon: 1 if the rows are equalised, 0 if the columns
+  kScal = 10
 };
 
 // One shape group as the kernels see it.
@@ -117,7 +125,8 @@ struct MatGroup {
   float* head_part;
   float* tail_part;
   float* rc_part;      // [count][tail_tiles][128]: per-tile row and column sums of O^2
-  float* rc_scale;     // [count][rows + cols]: row, then column scales of O
+  float* rc_scale;     // [count][rows + cols]: squared row, then column norms of O
+  float* rc_stat;      // [count][rc_chunks(rows, cols)][5]: per-chunk norm statistics
   float* scal;
   float* stats;        // MUON_STATS_PER_MATRIX per matrix, or null
   float decay;         // 1 - lr*wd
@@ -257,6 +266,7 @@ hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns
 hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
 // NorMuon / MeqMuon: row and column norms of O, the direction to equalise and
 // the per-row and per-column scales (one block per matrix).
+hipError_t launch_rc_sum(const Batch& bt, const Work& wk, hipStream_t s);
 hipError_t launch_rc_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
 // `reduced`: tail_finalize ran, so the per-matrix coefficient and MuonH
 // scale are read from the scalars (otherwise 0 and 1).

@@ -50,8 +50,8 @@ def test_status_strings(L):
 
 def ws_formula(count, rows, cols, dtype):
     """Workspace size from the layout the library documents (X0, X1, A, B,
-    head/tail partials, per-matrix scalars, row/column partials and scales;
-    256-byte aligned regions)."""
+    head/tail partials, per-matrix scalars (10), row/column partials, norms
+    and per-256-row/column chunk statistics (5); 256-byte aligned regions)."""
     tile_p, tile_q = (128, 256) if dtype == _lib.MUON_DTYPE_BF16 else (64, 64)
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     p, q = min(rows, cols), max(rows, cols)
@@ -59,9 +59,10 @@ def ws_formula(count, rows, cols, dtype):
     es = ES[dtype]
     head = (pp // 64) * (qp // 64)
     tail = math.ceil(rows / 64) * math.ceil(cols / 64)
+    chunks = math.ceil(rows / 256) + math.ceil(cols / 256)
     return (2 * al(count * pp * qp * es) + 2 * al(count * pp * pp * es) + al(count * head * 4)
-            + al(count * tail * 12) + al(count * 8 * 4) + al(count * tail * 128 * 4)
-            + al(count * (rows + cols) * 4) + 256)
+            + al(count * tail * 12) + al(count * 10 * 4) + al(count * tail * 128 * 4)
+            + al(count * (rows + cols) * 4) + al(count * chunks * 5 * 4) + 256)
 
 
 @pytest.mark.parametrize("shape", [(256, 512), (768, 3072), (3072, 768), (100, 300), (1, 1),

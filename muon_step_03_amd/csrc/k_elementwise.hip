@@ -462,20 +462,17 @@ __global__ __launch_bounds__(256) void rc_sum_kernel(Batch bt, Work wk) {
   }
 }
 
-// Second step, one block per matrix (one thread merges): the chunk
+// Second step, by one thread per matrix (in tail_finalize_kernel): the chunk
 // statistics of the rows and of the columns merged in chunk order (count,
 // mean and sum of squared deviations by the pairwise update of Chan et
 // al.), the direction to equalise (NorMuon: rows; MeqMuon: the one whose
 // norms have the larger std/mean, rows on a tie) and the common norm
 // target = ||O||_F / sqrt(count along it).  The apply kernel scales O by
 // target/norm along that direction (0 for a zero row or column).
-__global__ __launch_bounds__(64) void rc_finalize_kernel(Batch bt, Work wk, int variant) {
-  if (threadIdx.x != 0) return;
-  const TileRef tr = decode(bt, wk, blockIdx.x);
-  const MatGroup& g = *tr.g;
+__device__ void rc_merge(const MatGroup& g, int64_t m, int variant) {
   const int ncr = (g.rows + kRcChunk - 1) / kRcChunk;
   const int nch = rc_chunks(g.rows, g.cols);
-  const float* st = g.rc_stat + tr.m * nch * 5;
+  const float* st = g.rc_stat + m * nch * 5;
   float spread[2], sum_a[2], nz[2];
   for (int side = 0; side < 2; ++side) {
     const int c0 = side == 0 ? 0 : ncr, c1 = side == 0 ? ncr : nch;
@@ -495,15 +492,16 @@ __global__ __launch_bounds__(64) void rc_finalize_kernel(Batch bt, Work wk, int 
   }
   const bool rows_dir = variant == MUON_VARIANT_NORMUON || spread[0] >= spread[1];
   const float target = sqrtf(sum_a[0] / float(rows_dir ? g.rows : g.cols));
-  float* sc = g.scal + tr.m * kScal;
+  float* sc = g.scal + m * kScal;
   sc[SC_RC_TARGET] = target;
   sc[SC_RC_ROWS] = rows_dir ? 1.f : 0.f;
-  if (g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 4] = target * target * nz[rows_dir ? 0 : 1];
+  if (g.stats) g.stats[m * MUON_STATS_PER_MATRIX + 4] = target * target * nz[rows_dir ? 0 : 1];
 }
 
 // Per-matrix totals: ||W||^2, <W,O>, ||O||^2, the MuonGS coefficient and the
-// optional stats.
-__global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, int variant) {
+// optional stats; with rc (NorMuon, MeqMuon) also the equalisation's
+// direction and target (rc_sum_kernel ran before).
+__global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, int variant, int rc) {
   __shared__ float red[12];
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
@@ -537,6 +535,7 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
       st[3] = oo;
       st[4] = fmaxf(oo - 2.f * coef * dot + coef * coef * ww, 0.f);
     }
+    if (rc) rc_merge(g, tr.m, variant);
   }
 }
 
@@ -643,18 +642,13 @@ hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns
   return hipGetLastError();
 }
 
-hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s) {
-  hipLaunchKernelGGL(tail_finalize_kernel, grid_of(wk), dim3(256), 0, s, bt, wk, variant);
+hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, bool rc, hipStream_t s) {
+  hipLaunchKernelGGL(tail_finalize_kernel, grid_of(wk), dim3(256), 0, s, bt, wk, variant, int(rc));
   return hipGetLastError();
 }
 
 hipError_t launch_rc_sum(const Batch& bt, const Work& wk, hipStream_t s) {
   hipLaunchKernelGGL(rc_sum_kernel, grid_of(wk), dim3(256), 0, s, bt, wk);
-  return hipGetLastError();
-}
-
-hipError_t launch_rc_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s) {
-  hipLaunchKernelGGL(rc_finalize_kernel, grid_of(wk), dim3(64), 0, s, bt, wk, variant);
   return hipGetLastError();
 }
 

@@ -494,8 +494,8 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     if (reduce) {
       const bool rc = h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON;
       if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, rc, s), 5, s, t0))) return st;
-      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, s), 6, s, t0))) return st;
       if (rc) {
+        // row and column norms in blocks of kRcChunk rows or columns
         Work w_rc{};
         w_rc.ngroups = nsel;
         w_rc.begin[0] = 0;
@@ -504,9 +504,8 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
           w_rc.begin[k + 1] = w_rc.begin[k] + bt.g[k].count * w_rc.tiles[k];
         }
         if ((t0 = prof_start(s)), (st = finish_launch(launch_rc_sum(bt, w_rc, s), 6, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_rc_finalize(bt, w_one, h.variant, s), 6, s, t0)))
-          return st;
       }
+      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, rc, s), 6, s, t0))) return st;
     }
     if (w_tail.begin[nsel] > 0 &&  // every group may have been finished by its last update
         ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),

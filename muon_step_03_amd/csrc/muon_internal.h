@@ -263,11 +263,10 @@ hipError_t launch_norm_finalize(const Batch& bt, const Work& wk, hipStream_t s);
 // `rc`: also the per-tile row and column sums of O^2 (NorMuon, MeqMuon).
 hipError_t launch_tail_reduce(const Batch& bt, const Work& wk, bool bf16, int ns_steps, bool rc,
                               hipStream_t s);
-hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
+hipError_t launch_tail_finalize(const Batch& bt, const Work& wk, int variant, bool rc, hipStream_t s);
 // NorMuon / MeqMuon: row and column norms of O, the direction to equalise and
 // the per-row and per-column scales (one block per matrix).
 hipError_t launch_rc_sum(const Batch& bt, const Work& wk, hipStream_t s);
-hipError_t launch_rc_finalize(const Batch& bt, const Work& wk, int variant, hipStream_t s);
 // `reduced`: tail_finalize ran, so the per-matrix coefficient and MuonH
 // scale are read from the scalars (otherwise 0 and 1).
 hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const Hyper& h,

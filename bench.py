@@ -290,6 +290,19 @@ def main():
     ms_per_step = max(ev_ms, wall_ms) / args.steps
     print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
+    # ---- per-step distribution: the same K steps again, one event pair each
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    def pct(q):
+        return per_step_ms[min(len(per_step_ms) - 1, int(q * (len(per_step_ms) - 1) + 0.5))]
+
     work = matrix_work(w.groups, es)
     result = {
         "metric": METRIC, "value": 1e3 / ms_per_step, "unit": "steps/s", "n_gpus": 1,
@@ -303,6 +316,8 @@ def main():
                               else f"muon_step_grouped, {len(calls)} calls per step over "
                                    f"chunks of {calls[0][0].count} matrices per shape"),
                    "workspace_bytes": ws_bytes},
+        "step_ms": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
+                    "note": "a second pass of the same number of steps, one event pair per step"},
     }
 
     # ---- per-launch kernel times with HIP events on the launch stream

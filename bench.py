@@ -151,7 +151,8 @@ def cpu_baseline(wl_mod, w, seconds):
                 order.append((gi, k))
     spent = 0.0
     done = 0
-    for gi, k in order:
+    # cycle over the model until about `seconds` (at most 4 passes)
+    for gi, k in order * 4:
         g = w.groups[gi]
         gen = torch.Generator().manual_seed(10_000 + 131 * gi + k)
         W = (torch.randn(g.rows, g.cols, generator=gen) * 0.02).to(wl_mod.torch_dtype(w.dtype))
@@ -169,10 +170,17 @@ def cpu_baseline(wl_mod, w, seconds):
             break
     total = sum(g.count * (sum(per_shape[(g.rows, g.cols)]) / len(per_shape[(g.rows, g.cols)]))
                 for g in w.groups)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
     return {"value": 1.0 / total, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.n_matrices} matrices (round-robin over the shape groups), "
-                      f"{spent:.1f} s of fp64 NumPy; seconds/step extrapolated per shape",
-            "seconds_per_step": total, "host_cpus": os.cpu_count()}
+            "sample": f"{done} matrix steps over the {w.n_matrices} matrices (round-robin over the "
+                      f"shape groups, repeated up to 4 times), {spent:.1f} s of fp64 NumPy; "
+                      f"seconds/step = per-shape mean x count",
+            "seconds_per_step": total, "host_cpus": os.cpu_count(), "cpu_model": model}
 
 
 def aux_adamw(args, wl, dev, stream, muon_ms):

@@ -494,7 +494,9 @@ def recovered_o(W0, W1, shape, wd=0.1, lr=0.02):
     return -(f64(W1) - (1 - lr * wd) * f64(W0)) / step
 
 
-NORM_SHAPES = [(96, 256), (256, 96), (200, 200), (130, 70), (70, 130)]
+# the last two span several 256-row / 256-column chunks of the norm sums,
+# ragged on both sides
+NORM_SHAPES = [(96, 256), (256, 96), (200, 200), (130, 70), (70, 130), (300, 520), (600, 260)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) void rc_sum_kernel(Batch bt, Work wk) {
   const bool valid = idx < n;
   const int tcn = g.tail_tiles_c, trn = g.tail_tiles / g.tail_tiles_c;
   const float* part = g.rc_part + tr.m * g.tail_tiles * (2 * T);
-  float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
+  float* srow = g.rc_norm2 + tr.m * (int64_t(g.rows) + g.cols);
   float* scol = srow + g.rows;
   float a = 0.f;
   if (valid) {
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256) void tail_apply_kernel(Batch bt, Work wk, int 
     // direction (0 for a zero row or column), by 1 along the other; indices
     // clamped so that a ragged tile reads inside the matrix's norms (the
     // clamped products are never stored).
-    const float* srow = g.rc_scale + tr.m * (int64_t(g.rows) + g.cols);
+    const float* srow = g.rc_norm2 + tr.m * (int64_t(g.rows) + g.cols);
     const float* scol = srow + g.rows;
     // (both sets of norms loaded unconditionally, beside the two scalars,
     // so that no load waits for another)

@@ -384,7 +384,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       base += L.scal_bytes;
       m.rc_part = reinterpret_cast<float*>(base);
       base += L.rc_bytes;
-      m.rc_scale = reinterpret_cast<float*>(base);
+      m.rc_norm2 = reinterpret_cast<float*>(base);
       base += L.rcs_bytes;
       m.rc_stat = reinterpret_cast<float*>(base);
       base += L.rcst_bytes;

@@ -125,7 +125,7 @@ struct MatGroup {
   float* head_part;
   float* tail_part;
   float* rc_part;      // [count][tail_tiles][128]: per-tile row and column sums of O^2
-  float* rc_scale;     // [count][rows + cols]: squared row, then column norms of O
+  float* rc_norm2;     // [count][rows + cols]: squared row, then column norms of O
   float* rc_stat;      // [count][rc_chunks(rows, cols)][5]: per-chunk norm statistics
   float* scal;
   float* stats;        // MUON_STATS_PER_MATRIX per matrix, or null

@@ -1,0 +1,66 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the algorithmic work
+per step against the budget table of the workloads (NS flops N*sum(3p^2q +
+p^3), elementwise bytes 12 + 6 per bf16 element), and the traffic figure's
+guard on the kernel sources."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from muon_step_03_amd import workloads as wl  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+# (workload, NS algorithmic TFLOP per step, elementwise GB per step): the
+# per-configuration budget of the workloads (five iterations; head 12 and
+# tail 6 bytes per bf16 element)
+BUDGET = [("gpt160m", 1.142, 1.529), ("gpt400m", 5.412, 5.436), ("moe1b", 26.167, 54.585),
+          ("stress2k", 813.6, 425.2)]
+
+
+@pytest.mark.parametrize("name,tflop,gb", BUDGET)
+def test_algorithmic_work_matches_budget(name, tflop, gb):
+    w = wl.WORKLOADS[name]
+    work = bench.matrix_work(w.groups, 2)
+    ns = 5 * (work["gram"] + work["poly"] + work["update"])
+    assert ns / 1e12 == pytest.approx(tflop, rel=1e-3)
+    assert (work["head_bytes"] + work["tail_bytes"]) / 1e9 == pytest.approx(gb, rel=1e-3)
+
+
+def test_matrix_work_closed_form():
+    """One 256x512 and one 512x256 matrix: p = 256, q = 512 for both."""
+    class G:
+        def __init__(self, count, rows, cols):
+            self.count, self.rows, self.cols = count, rows, cols
+    work = bench.matrix_work([G(1, 256, 512), G(1, 512, 256)], 4)
+    p, q = 256, 512
+    assert work["gram"] == 2 * p * p * q
+    assert work["poly"] == 2 * p ** 3
+    assert work["update"] == 2 * 2 * p * p * q
+    assert work["head_bytes"] == 2 * p * q * 16      # fp32: G r 4, M r 4 + w 4, X0 w 4
+    assert work["tail_bytes"] == 2 * p * q * 12
+
+
+def test_traffic_figure_needs_matching_sources(tmp_path, monkeypatch):
+    """The committed counter summary is used only while the kernel sources
+    hash to the value recorded with it."""
+    f = tmp_path / "traffic.md"
+    f.write_text("traffic_bytes_per_launch: 123456\n"
+                 f"kernel_source_sha256: `{bench.kernel_source_hash()}`\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("gpt160m") == 123456
+    assert bench.measured_traffic("gpt400m") is None
+    f.write_text("traffic_bytes_per_launch: 123456\nkernel_source_sha256: `0000`\n")
+    assert bench.measured_traffic("gpt160m") is None

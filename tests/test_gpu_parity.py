@@ -387,16 +387,24 @@ def test_gpt160m_full_set(variant, with_stats):
 
 
 def test_gpt400m_consecutive_steps():
-    """Three consecutive Muon and MuonGS steps with fresh gradients; each step
-    graded against the oracle from the GPU's own W_t, M_t (teacher forcing)."""
+    """Ten consecutive Muon and MuonGS steps with a fresh gradient every step
+    (the GPT-400M configuration); steps 0, 4 and 9 graded against the oracle
+    from the GPU's own W_t, M_t (teacher forcing), with the MuonGS invariants
+    on those steps; every step leaves W and M finite."""
     w = wl.WORKLOADS["gpt400m"]
     for variant in ("muon", "muongs"):
         Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
-        for step in range(3):
+        for step in range(10):
             W0, Gs, M0 = run_workload(w, step, Ws, Ms, variant)
+            assert all(bool(torch.isfinite(x).all()) for x in Ws + Ms), step
+            if step not in (0, 4, 9):
+                continue
             for gi, i in sampled(w, per_group=1):
                 e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i],
                                                Ms[gi][i], variant=variant)
+                if variant == "muongs":
+                    check_muongs_invariants(W0[gi][i], Ws[gi][i], 0.02, 0.1, cos_tol=1e-3,
+                                            r2_tol=1e-3)
                 print(f"gpt400m step {step} {w.groups[gi]} {variant}: relF(dW) = {e:.2e}")
 
 

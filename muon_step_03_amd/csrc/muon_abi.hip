@@ -431,8 +431,8 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       }
       const bool use_big_syrk = big_syrk >= int64_t(kSyrkBigMinRounds) * 8 * cpx;
       const bool use_big_upd = big_upd >= int64_t(kUpdBigMinRounds) * 8 * cpx;
-      int64_t nt[kMaxGroups], ntb[kMaxGroups], nu[kMaxGroups], nub[kMaxGroups], kq[kMaxGroups],
-          kp[kMaxGroups];
+      int64_t nt[kMaxGroups], ntb[kMaxGroups], npt[kMaxGroups], nptb[kMaxGroups], nu[kMaxGroups],
+          nub[kMaxGroups], kq[kMaxGroups], kp[kMaxGroups];
       for (int k = 0; k < nsel; ++k) {
         const Layout& L = sel[k].L;
         const bool elig = big_eligible(L, true);
@@ -440,15 +440,23 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
         const int64_t nb = L.p_pad / kBigTile;
         nt[k] = big ? 0 : w_gram.tiles[k];
         ntb[k] = big ? nb * (nb + 1) / 2 : 0;
+        // the polynomial (K = p) keeps 128-wide tiles below kPolyBigMinP:
+        // one 256x256 tile's epilogue moves 512 KiB (B, its mirror, b*A
+        // for both) with no second block on the CU to overlap it, which
+        // short contractions do not amortise (measured: p = 512 and 1024
+        // faster in 128-wide tiles, p = 2048 in 256-wide)
+        const bool pbig = big && L.p >= kPolyBigMinP;
+        npt[k] = pbig ? 0 : w_gram.tiles[k];
+        nptb[k] = pbig ? nb * (nb + 1) / 2 : 0;
         nu[k] = ubig ? 0 : w_upd.tiles[k];
         nub[k] = ubig ? nb * (L.q_pad / kBigTile) : 0;
         kq[k] = bt.g[k].q_pad;
         kp[k] = bt.g[k].p_pad;
       }
       tl_gram = make_tile_list(bt, nt, kq, kSyrkBlocksPerCU * cpx);
-      tl_poly = make_tile_list(bt, nt, kp, kSyrkBlocksPerCU * cpx);
+      tl_poly = make_tile_list(bt, npt, kp, kSyrkBlocksPerCU * cpx);
       tl_gram_big = make_tile_list(bt, ntb, kq, kBigBlocksPerCU * cpx);
-      tl_poly_big = make_tile_list(bt, ntb, kp, kBigBlocksPerCU * cpx);
+      tl_poly_big = make_tile_list(bt, nptb, kp, kBigBlocksPerCU * cpx);
       tl_upd = make_tile_list(bt, nu, kp, kUpdBlocksPerCU * cpx);
       tl_upd_big = make_tile_list(bt, nub, kp, kBigBlocksPerCU * cpx);
     }

@@ -69,6 +69,11 @@ constexpr int kSyrkTile = MUON_SYRK_TILE;   // symmetric products: square tiles
 constexpr int kBigTile = 256;
 constexpr int kBigMinP = MUON_SYRK_BIG_MIN_P;
 constexpr int kBigBlocksPerCU = 1;
+// Short side from which the polynomial also takes 256x256 tiles.
+#ifndef MUON_POLY_BIG_MIN_P
+#define MUON_POLY_BIG_MIN_P 2048
+#endif
+constexpr int kPolyBigMinP = MUON_POLY_BIG_MIN_P;
 #ifndef MUON_SYRK_BIG_MIN_ROUNDS
 #define MUON_SYRK_BIG_MIN_ROUNDS 4
 #endif

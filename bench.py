@@ -123,7 +123,9 @@ def matrix_work(groups, dtype_bytes):
         upd += g.count * 2.0 * p * p * q       # B X
         elems += g.count * g.rows * g.cols
     es = dtype_bytes
-    return dict(gram=gram, poly=poly, update=upd, elems=elems,
+    upd_bytes = sum(g.count * (min(g.rows, g.cols) ** 2 + 2 * g.rows * g.cols) * dtype_bytes
+                    for g in groups)                      # B r, X r, X' w
+    return dict(gram=gram, poly=poly, update=upd, elems=elems, update_bytes=upd_bytes,
                 head_bytes=elems * (es + 4 + 4 + es),   # G r, M r+w, X0 w
                 tail_bytes=elems * (es + es + es))      # W r, O r, W w
 
@@ -357,6 +359,17 @@ def main():
             "achieved": a / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s", "frac": a / peak,
             "traffic": measured_traffic(w.name), "avg_launch_ms": avg["update"],
             "alg_flops_per_launch": upd_flops,
+        }
+        # The same launch against the HBM roofline: its algorithmic bytes
+        # (B and X read once, X' written once, unpadded shapes) over the
+        # same time, and the arithmetic intensity against the ridge point
+        # (dense bf16 peak / HBM peak = 312 flop/byte).
+        upd_bytes = work["update_bytes"] * upd_iters / per["update"]
+        result["roofline"]["hbm_view"] = {
+            "alg_bytes_per_launch": upd_bytes,
+            "gbps": upd_bytes / (avg["update"] * 1e-3) / 1e9,
+            "frac_of_hbm": upd_bytes / (avg["update"] * 1e-3) / PEAK_HBM,
+            "flop_per_byte": upd_flops / upd_bytes, "ridge_flop_per_byte": peak / PEAK_HBM,
         }
         # The last update of a step may also apply the step to W (plain Muon
         # without statistics, bf16): it is timed as its own phase, so

@@ -51,6 +51,7 @@ def test_matrix_work_closed_form():
     assert work["update"] == 2 * 2 * p * p * q
     assert work["head_bytes"] == 2 * p * q * 16      # fp32: G r 4, M r 4 + w 4, X0 w 4
     assert work["tail_bytes"] == 2 * p * q * 12
+    assert work["update_bytes"] == 2 * (p * p + 2 * p * q) * 4   # B r, X r, X' w
 
 
 def test_traffic_figure_needs_matching_sources(tmp_path, monkeypatch):

@@ -328,7 +328,7 @@ def test_transpose_equivariance(dtype):
     assert relF(f64(W2).T - f64(W), f64(W1) - f64(W)) <= tol
 
 
-@pytest.mark.parametrize("variant", ["muon", "muongs"])
+@pytest.mark.parametrize("variant", ["muon", "muongs", "muonh", "normuon", "meqmuon"])
 def test_workspace_contents_do_not_matter(variant):
     """The step must not read workspace it has not written: a zeroed and a
     NaN-filled workspace (0xFF bytes) give bitwise identical results on the

@@ -69,6 +69,44 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _keep_for_stream(stream, *tensors) -> None:
+    """Tensors this binding allocated (on the current stream) and hands to
+    kernels enqueued on ``stream``: when that is another stream, tell the
+    caching allocator, so that their blocks are not given to a later
+    allocation before the kernels on ``stream`` are done with them."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream(stream.device)
+    if stream.cuda_stream == cur.cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def check_stats(stats, n_matrices: int, device=None) -> None:
+    """A statistics buffer must be a contiguous float32 GPU tensor of at least
+    ``n_matrices * MUON_STATS_PER_MATRIX`` elements (on ``device`` if given):
+    the library writes that many floats and no bounds are checked on the
+    device."""
+    if stats is None:
+        return
+    if not isinstance(stats, torch.Tensor):
+        raise TypeError("stats must be a torch.Tensor")
+    need = int(n_matrices) * _lib.MUON_STATS_PER_MATRIX
+    if stats.dtype != torch.float32:
+        raise ValueError(f"stats must be float32, got {stats.dtype}")
+    if stats.numel() < need:
+        raise ValueError(f"stats holds {stats.numel()} floats, {need} needed "
+                         f"({n_matrices} matrices x {_lib.MUON_STATS_PER_MATRIX})")
+    if not stats.is_contiguous():
+        raise ValueError("stats must be contiguous")
+    if not stats.is_cuda:
+        raise ValueError("stats must be on a GPU")
+    if device is not None and stats.device != torch.device(device):
+        raise ValueError(f"stats is on {stats.device}, the weights on {device}")
+
+
 def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
@@ -136,13 +174,14 @@ def muon_step(W, G, M, *, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
     dt = dtype_code(W.dtype)
     need = workspace_bytes(1, rows, cols, W.dtype)
     ws = _workspace(need, W.device, workspace)
-    if stats is not None and (stats.dtype != torch.float32 or stats.numel() < 5 or not stats.is_cuda):
-        raise ValueError("stats must be a float32 GPU tensor with at least 5 elements")
+    check_stats(stats, 1, W.device)
     st = _lib.lib().muon_step(
         _ptr(W), _ptr(G), _ptr(M), rows, cols,
         *_scalars(dt, lr, momentum, weight_decay, ns_steps, ns_coefficients, variant, scale),
         _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
     _check(st, "muon_step")
+    if workspace is None:
+        _keep_for_stream(stream, ws)
     return W, M
 
 
@@ -170,8 +209,10 @@ def muon_step_batched(Ws, Gs, Ms, *, lr=0.02, momentum=0.95, weight_decay=0.1, n
         _check_matrix(f"G[{i}]", g, shape, dtype)
         _check_matrix(f"M[{i}]", m, shape, torch.float32)
     dev = Ws[0].device
-    if tables is None:
+    own_tables = tables is None
+    if own_tables:
         tables = (pointer_table(Ws, dev), pointer_table(Gs, dev), pointer_table(Ms, dev))
+    check_stats(stats, len(Ws), dev)
     rows, cols = shape
     need = workspace_bytes(len(Ws), rows, cols, dtype)
     ws = _workspace(need, dev, workspace)
@@ -181,6 +222,7 @@ def muon_step_batched(Ws, Gs, Ms, *, lr=0.02, momentum=0.95, weight_decay=0.1, n
                   variant, scale),
         _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
     _check(st, "muon_step_batched")
+    _keep_for_stream(stream, *(tables if own_tables else ()), ws if workspace is None else None)
 
 
 def stacked_group(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor) -> _lib.MuonGroup:
@@ -258,6 +300,7 @@ def muon_step_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, l
     need = workspace_bytes_grouped(groups, dtype)
     if device is None:
         device = torch.device("cuda", torch.cuda.current_device())
+    check_stats(stats, sum(int(g.count) for g in groups), device)
     ws = _workspace(need, device, workspace)
     arr = _groups_array(groups)
     st = _lib.lib().muon_step_grouped(
@@ -266,6 +309,8 @@ def muon_step_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, l
                   variant, scale),
         _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream_handle(stream))
     _check(st, "muon_step_grouped")
+    if workspace is None:
+        _keep_for_stream(stream, ws)
 
 
 class MuonStep:
@@ -273,7 +318,13 @@ class MuonStep:
 
     Parameters are grouped by (shape, dtype); each group keeps device pointer
     tables and fp32 momentum buffers, and :meth:`step` updates every group in
-    one launch sequence per dtype from the parameters' ``.grad``.
+    one launch sequence per dtype from the parameters' ``.grad``, on the
+    current stream.
+
+    ``stats_order`` lists the parameter indices in the order of the rows of
+    the optional ``stats`` buffer of :meth:`step` (``MUON_STATS_PER_MATRIX``
+    floats per parameter): parameters grouped by dtype, then by shape (each
+    in order of first appearance), then in parameter order.
     """
 
     def __init__(self, params, lr=0.02, momentum=0.95, weight_decay=0.1, ns_steps=5,
@@ -291,36 +342,49 @@ class MuonStep:
         self._by_dtype = {}
         for i, p in enumerate(self.params):
             self._by_dtype.setdefault(p.dtype, {}).setdefault(tuple(p.shape), []).append(i)
+        self.stats_order = [i for shapes in self._by_dtype.values() for idx in shapes.values()
+                            for i in idx]
         self._tables = {}
         self._workspaces = {}
+
+    def _table(self, tab, slot, tensors, dev):
+        """Rebuild the pointer table in ``tab[slot]`` when the tensors' data
+        pointers differ from the ones it was built from (``tab[slot + 1]``):
+        a parameter whose ``.data`` was rebound, or new gradient tensors."""
+        ptrs = tuple(t.data_ptr() for t in tensors)
+        if tab[slot + 1] != ptrs:
+            tab[slot] = pointer_table(tensors, dev)
+            tab[slot + 1] = ptrs
+        return tab[slot]
 
     def _groups(self, dtype, shapes):
         groups, keep = [], []
         for shape, idx in shapes.items():
             dev = self.params[idx[0]].device
-            grads = []
+            grads, datas = [], []
             for i in idx:
                 g = self.params[i].grad
                 if g is None:
                     raise RuntimeError(f"parameter {i} has no gradient")
                 _check_matrix(f"grad[{i}]", g, shape, dtype)
+                _check_matrix(f"param[{i}]", self.params[i].data, shape, dtype)
                 grads.append(g)
-            key = (dtype, shape)
-            if key not in self._tables:
-                self._tables[key] = [pointer_table([self.params[i].data for i in idx], dev), None,
-                                     pointer_table([self.momentum_buffers[i] for i in idx], dev),
-                                     None]
-            tab = self._tables[key]
-            gptrs = tuple(g.data_ptr() for g in grads)
-            if tab[3] != gptrs:
-                tab[1] = pointer_table(grads, dev)
-                tab[3] = gptrs
-            groups.append(table_group(len(idx), shape[0], shape[1], tab[0], tab[1], tab[2]))
+                datas.append(self.params[i].data)
+            tab = self._tables.setdefault((dtype, shape), [None] * 6)
+            w_tab = self._table(tab, 0, datas, dev)
+            g_tab = self._table(tab, 2, grads, dev)
+            m_tab = self._table(tab, 4, [self.momentum_buffers[i] for i in idx], dev)
+            groups.append(table_group(len(idx), shape[0], shape[1], w_tab, g_tab, m_tab))
             keep.append(grads)
         return groups, keep
 
     @torch.no_grad()
     def step(self, stats=None):
+        """One step of every parameter.  ``stats``: optional float32 GPU
+        tensor of ``len(params) * MUON_STATS_PER_MATRIX`` floats, rows in
+        ``stats_order``."""
+        check_stats(stats, len(self.params))
+        offset = 0
         for dtype, shapes in self._by_dtype.items():
             groups, _keep = self._groups(dtype, shapes)
             need = workspace_bytes_grouped(groups, dtype)
@@ -329,8 +393,11 @@ class MuonStep:
                 dev = self.params[next(iter(shapes.values()))[0]].device
                 ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
                 self._workspaces[dtype] = ws
-            muon_step_grouped(groups, dtype, workspace=ws, stats=stats, device=ws.device,
-                              **self.hp)
+            n = sum(len(idx) for idx in shapes.values())
+            st = None if stats is None else \
+                stats[offset * _lib.MUON_STATS_PER_MATRIX:(offset + n) * _lib.MUON_STATS_PER_MATRIX]
+            muon_step_grouped(groups, dtype, workspace=ws, stats=st, device=ws.device, **self.hp)
+            offset += n
 
 
 # ---------------------------------------------------------------- AdamW half

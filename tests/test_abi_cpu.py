@@ -301,3 +301,22 @@ def test_chunk_size_whole_model_and_errors():
         chunk_size(shapes, torch.bfloat16, _need(shapes, 1) - 1)
     with pytest.raises(ValueError):
         chunk_size([], torch.bfloat16, 1 << 30)
+
+
+def test_stats_buffer_checks():
+    """The binding refuses a statistics buffer the library would write past
+    (MUON_STATS_PER_MATRIX floats per matrix, no bounds on the device), of the
+    wrong dtype, non-contiguous or on the host."""
+    import torch
+    from muon_step_03_amd.api import check_stats
+    check_stats(None, 7)
+    with pytest.raises(ValueError, match="needed"):
+        check_stats(torch.zeros(2 * _lib.MUON_STATS_PER_MATRIX - 1), 2)
+    with pytest.raises(ValueError, match="float32"):
+        check_stats(torch.zeros(10, dtype=torch.float64), 2)
+    with pytest.raises(ValueError, match="contiguous"):
+        check_stats(torch.zeros(20)[::2], 2)
+    with pytest.raises(ValueError, match="GPU"):
+        check_stats(torch.zeros(10), 2)
+    with pytest.raises(TypeError):
+        check_stats([0.0] * 10, 2)

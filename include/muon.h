@@ -5,8 +5,8 @@
  * One Muon call performs one optimizer step on 2-D hidden-layer weight matrices:
  *
  *   M' = mu*M + G;  U = G + mu*M'                 momentum, Nesterov look-ahead
- *   X0 = U / (||U||_F + 1e-7)                     (U^T first if rows > cols)
- *   repeat ns_steps:  A = X X^T;  B = b*A + c*A*A;  X = a*X + B*X
+ *   X0 = U scaled by 1 / (||U||_F + eps), eps = 1e-7   (U^T first if rows > cols)
+ *   ns_steps times:  X <- a X + b (X X^T) X + c (X X^T)^2 X
  *   O  = X (transposed back if rows > cols)
  *   O~ = O - (<W,O>_F / ||W||_F^2) W              MuonGS only, when ||W|| > 0
  *   W' = (1 - lr*wd) W - lr * 0.2*sqrt(max(rows,cols)) * O~
@@ -15,9 +15,9 @@
  *  - update order: "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저"
  *    (codersblog.github.io), section 3 "Muon의 업데이트 순서", steps 1-5;
  *  - momentum 0.95 / Nesterov / 5 steps / coefficients (3.4445, -4.7750, 2.0315)
- *    / 1e-7: "LLM Pretraining Loss Spike 진단과 처방 ... Muon 전환 판단"
- *    (juhoplayground.github.io), section "Muon head의 실체는 하이브리드
- *    옵티마이저다", Newton-Schulz code block and the defaults after it;
+ *    / the norm's stabiliser eps: "LLM Pretraining Loss Spike 진단과 처방 ...
+ *    Muon 전환 판단" (juhoplayground.github.io), section "Muon head의 실체는
+ *    하이브리드 옵티마이저다", its Newton-Schulz snippet and the defaults after it;
  *  - the iteration X_k = aX + b(XX^T)X + c(XX^T)^2 X approximating
  *    (MM^T)^{-1/2}M and the 0.2*sqrt(max(A,B)) scale (eq. 4): "[논문 AI 리뷰]
  *    MUON IS SCALABLE FOR LLM TRAINING TECHNICAL REPORT" (blog.pieroot.xyz),

@@ -50,9 +50,10 @@ from __future__ import annotations
 import numpy as np
 
 # [LS] section "Muon head의 실체는 하이브리드 옵티마이저다", the Newton-Schulz
-# code block: the quintic coefficients as printed (a, b, c).
+# snippet: the quintic coefficients as printed (a, b, c).
 NS_COEFFICIENTS = (3.4445, -4.7750, 2.0315)
-# Same code block: the stabiliser added to the Frobenius norm.
+# Same snippet: the small constant added to the Frobenius norm before the
+# first iterate is scaled by its reciprocal.
 NS_EPS = 1e-7
 # [LS] same section, the listed defaults: lr 0.02, momentum 0.95 (Nesterov),
 # ns_steps 5.  Weight decay 0.1 is [MX] section 5's example.
@@ -104,16 +105,18 @@ def nesterov_momentum(G, M, momentum):
 def newton_schulz(U, a, b, c, steps, eps=NS_EPS):
     """Approximate the orthogonal polar factor (U U^T)^{-1/2} U.
 
-    [LS] Newton-Schulz code block and [MS] section 2: starting from
-    X_0 = U / (||U||_F + eps), repeat ``steps`` times
+    [MS] section 2: the iteration X_k = a X + b (X X^T) X + c (X X^T)^2 X,
+    evaluated term by term as written there, with P = X X^T:
 
-        A = X X^T
-        B = b*A + c*A A
-        X = a*X + B X
+        Y = P X          the cubic term  (X X^T) X
+        Z = P Y          the quintic term (X X^T)^2 X
+        X <- a X + b Y + c Z
 
-    which is X_k = a X + b (X X^T) X + c (X X^T)^2 X.  The iteration runs on
-    the shorter side ([MX] section 2): a tall U (rows > cols) is transposed
-    before and after.  ``steps == 0`` returns the normalised X_0.
+    The start X_0 is U divided by its Frobenius norm plus the small constant
+    NS_EPS (the [LS] Newton-Schulz snippet normalises this way, with that
+    stabiliser added to the norm).  The iteration runs on the shorter
+    side ([MX] section 2): a tall U (rows > cols) is transposed before and
+    after.  ``steps == 0`` returns the scaled X_0.
     """
     U = _f64(U)
     if U.ndim != 2:
@@ -122,9 +125,10 @@ def newton_schulz(U, a, b, c, steps, eps=NS_EPS):
     X = U.T if transposed else U
     X = X / (np.linalg.norm(X, "fro") + eps)
     for _ in range(steps):
-        A = X @ X.T
-        B = b * A + c * (A @ A)
-        X = a * X + B @ X
+        P = X @ X.T
+        Y = P @ X
+        Z = P @ Y
+        X = a * X + b * Y + c * Z
     return X.T if transposed else X
 
 

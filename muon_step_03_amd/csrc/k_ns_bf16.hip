@@ -5,13 +5,15 @@
 // One iteration, on X (p x q, short side first):
 //   A = X X^T                 symmetric: only lower-triangle block tiles are
 //                             computed, each written to both triangles
-//   B = b*A + c*A A^T         A is symmetric, so A A = A A^T: the same
-//                             symmetric form with K = p and the b*A epilogue
-//   X' = a*X + B X            full p x q output
-// which is X_k = aX + b(XX^T)X + c(XX^T)^2 X of "[논문 AI 리뷰] MUON IS
-// SCALABLE FOR LLM TRAINING TECHNICAL REPORT", section 2, and the three-line
-// Newton-Schulz code block of "LLM Pretraining Loss Spike 진단과 처방 ... Muon
-// 전환 판단", section "Muon head의 실체는 하이브리드 옵티마이저다".
+//   B = a*I + b*A + c*A A^T   A is symmetric, so A A = A A^T: the same
+//                             symmetric form with K = p; b*A and a*I are
+//                             added in the fp32 epilogue
+//   X' = B X                  full p x q output, a plain product
+// which is X_k = aX + b(XX^T)X + c(XX^T)^2 X = (aI + bA + cA^2) X of "[논문
+// AI 리뷰] MUON IS SCALABLE FOR LLM TRAINING TECHNICAL REPORT", section 2.
+// Holding a*I in the stored polynomial (one more term on its diagonal tiles)
+// spares the update an epilogue pass that would read its X tile a second
+// time: the largest source of the update's re-read traffic.
 //
 // The first iteration receives the unnormalised U (the head cannot know
 // ||U|| while it writes X0): its Gram is scaled by inv^2 and its update by
@@ -39,9 +41,9 @@
 //    LDS address is a lane's base plus an immediate: the loop body issues
 //    MFMAs, LDS reads and loads with almost no vector address arithmetic.
 //  * Epilogue: the fp32 tile is staged through LDS in 64-row passes and
-//    stored as 16-byte rows of 8 bf16; the linear terms (a*X of the update,
-//    b*A of the polynomial) are read there as 16-byte rows of the operand
-//    (L2-resident), so the K loop carries nothing but the product.
+//    stored as 16-byte rows of 8 bf16; the polynomial's linear term b*A is
+//    read there as 16-byte rows of A (L2-resident), so the K loop carries
+//    nothing but the product.
 //  * K-contiguous operand tiles: rows of BK bf16 (4 or 8 chunks of 16 B),
 //    chunk c of row m stored at c ^ f(m), f(m) = ((m>>1) + (m>>3)) & 3 for
 //    4 chunks, (m>>1) & 7 for 8, so the fragment reads (32 consecutive rows,
@@ -222,7 +224,7 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
 
 template <int MODE, class C>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
-    Batch bt, TileList tl, int iter, float c1, float c2) {
+    Batch bt, TileList tl, int iter, float ca, float cb, float cc) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES, BK = C::BK;
   constexpr int KS = BK / 16;                        // MFMA sub-steps per K step
   constexpr int CPK = BK / 8;                        // 16-byte chunks per operand row
@@ -239,7 +241,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   static_assert((S - 1) * LOADS < 64, "vmcnt field");
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE_BYTES];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
-  (void)c2;
+  (void)ca;
+  (void)cb;
+  (void)cc;
 
   // Persistent blocks: XCD x (= blockIdx % 8, the hardware's round-robin)
   // owns the contiguous slice [n x/8, n (x+1)/8) of every group's n tiles,
@@ -526,13 +530,13 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   }
   const bool mirror = (MODE != MODE_UPDATE) && (ti != tj);
   // Final values in fp32, before one rounding: Gram alpha*(X X^T),
-  // polynomial c*(A A) + b*A, update alpha*(a*X + B X).
+  // polynomial c*(A A) + b*A + a*I, update alpha*(B X).
 #pragma unroll
   for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= (MODE == MODE_POLY ? c2 : alpha);
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= (MODE == MODE_POLY ? cc : alpha);
   // fp32 staging row pitch (floats): 4 mod 64 banks, so the 16-byte writes of
   // 16 lanes (16 consecutive rows, one column) cover all banks once.
   constexpr int TP = BN + 4;
@@ -615,14 +619,13 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     for (int e = 0; e < 4; ++e) w[e] = f2bf2(v[2 * e], v[2 * e + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   };
-  // The linear term of the update (alpha*a*X) and of the polynomial (b*A)
-  // at the output positions, read as 16-byte rows of the operand the tile
-  // was computed from (L2-resident: its K steps just streamed through).  A
+  // The polynomial's linear term b*A at the output positions, read as
+  // 16-byte rows of A (L2-resident: its K steps just streamed through).  A
   // is symmetric, so a mirrored chunk's term is again a row segment of A.
-  constexpr bool kLin = MODE != MODE_GRAM;
+  constexpr bool kLin = MODE == MODE_POLY;
   constexpr int MCH = BN * 8 / NT;           // mirrored chunks per thread per pass
-  const uint16_t* Lin = MODE == MODE_UPDATE ? Xin : Am;
-  const float lin_coef = MODE == MODE_UPDATE ? alpha * c1 : c1;
+  const uint16_t* Lin = Am;
+  const float lin_coef = cb;
   auto add_lin = [&](float (&v)[8], const uint4& x) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -746,12 +749,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     static_assert(CHUNKS % GS == 0, "chunk groups");
 #pragma unroll
     for (int u0 = 0; u0 < CHUNKS; u0 += GS) {
-      uint4 lin[GS], wv[GS];
+      uint4 wv[GS];
 #pragma unroll
       for (int u = 0; u < GS; ++u) {
         const int q = t + NT * (u0 + u);
         const int row = q / CPR, col = (q % CPR) * 8;
-        lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
         const int i = i0 + 64 * pass + row, j = j0 + col;
         wv[u] = make_uint4(0, 0, 0, 0);
         if (!g.trans && wvec && i < g.p && j < g.q)
@@ -769,7 +771,6 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
           v[e] = v0[e];
           v[e + 4] = v1[e];
         }
-        add_lin(v, lin[u]);
         const int i = i0 + 64 * pass + row, j = j0 + col;
         if (!g.trans) {
           if (i < g.p && j < g.q) {
@@ -833,18 +834,23 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 
 #pragma unroll
   for (int pass = 0; pass < BM / 64; ++pass) {
-    // The linear terms' loads are issued before the pass's staging and
-    // barriers where registers allow (the polynomial of 64x64 wave tiles,
-    // and every 256x256 tile: its one block per CU has no other block to
-    // hide their latency behind; MoE-1B update 19.4 -> 18.7 ms per step);
-    // the 4-wave update issues them after the staging.  The fused last
-    // update loads its own.
+    // The polynomial's b*A loads are issued before the pass's staging and
+    // barriers where registers allow (64x64 wave tiles, and the 256x256
+    // tiles, whose one block per CU has no other block to hide their latency
+    // behind), after the staging otherwise.
     uint4 lin[kLin ? CHUNKS : 1], lin_m[kLin ? MCH : 1];
-    constexpr bool kEarlyLin = (MODE == MODE_POLY && WM * WN <= 4) || (C::NW == 8 && MODE != MODE_GRAM);
+    constexpr bool kEarlyLin = kLin && (WM * WN <= 4 || C::NW == 8);
     if (kEarlyLin && !fuse) load_lin(pass, lin, lin_m);
     block_barrier();  // stage buffers (pass 0) / the previous pass's T no longer read
     stage(pass);
     block_barrier();
+    if (MODE == MODE_POLY && ti == tj) {
+      // a*I on a diagonal tile (i0 == j0): staged row r of this pass holds
+      // its diagonal element in column 64 pass + r; the padding rows beyond
+      // p keep a zero diagonal
+      if (t < 64 && i0 + 64 * pass + t < g.p) T[t * TP + 64 * pass + t] += ca;
+      block_barrier();
+    }
     if (fuse) {
       finish_tail(pass);
     } else {
@@ -874,29 +880,29 @@ inline dim3 grid_of(const TileList& tl) { return dim3(unsigned(8 * tl.blocks_per
 hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s) {
   if (big)
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_GRAM, CfgSyrkBig>), grid_of(tl), dim3(64 * CfgSyrkBig::NW),
-                       0, s, bt, tl, iter, 0.f, 0.f);
+                       0, s, bt, tl, iter, 0.f, 0.f, 0.f);
   else
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_GRAM, Cfg<MODE_GRAM>>), grid_of(tl),
-                       dim3(64 * Cfg<MODE_GRAM>::NW), 0, s, bt, tl, iter, 0.f, 0.f);
+                       dim3(64 * Cfg<MODE_GRAM>::NW), 0, s, bt, tl, iter, 0.f, 0.f, 0.f);
   return hipGetLastError();
 }
-hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, bool big, hipStream_t s) {
+hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float a, float b, float c, bool big,
+                            hipStream_t s) {
   if (big)
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_POLY, CfgSyrkBig>), grid_of(tl), dim3(64 * CfgSyrkBig::NW),
-                       0, s, bt, tl, 0, b, c);
+                       0, s, bt, tl, 0, a, b, c);
   else
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_POLY, Cfg<MODE_POLY>>), grid_of(tl),
-                       dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, b, c);
+                       dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, a, b, c);
   return hipGetLastError();
 }
-hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, bool big,
-                              hipStream_t s) {
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s) {
   if (big)
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, CfgUpdBig>), grid_of(tl), dim3(64 * CfgUpdBig::NW),
-                       0, s, bt, tl, iter, a, 0.f);
+                       0, s, bt, tl, iter, 0.f, 0.f, 0.f);
   else
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, Cfg<MODE_UPDATE>>), grid_of(tl),
-                       dim3(64 * Cfg<MODE_UPDATE>::NW), 0, s, bt, tl, iter, a, 0.f);
+                       dim3(64 * Cfg<MODE_UPDATE>::NW), 0, s, bt, tl, iter, 0.f, 0.f, 0.f);
   return hipGetLastError();
 }
 

@@ -478,11 +478,11 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
             ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram_big, it, true, s), 2, s, t0))))
           return st;
         if (tl_poly.ngroups &&
-            ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.b, h.c, false, s), 3, s, t0))))
+            ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.a, h.b, h.c, false, s), 3, s, t0))))
           return st;
         if (tl_poly_big.ngroups &&
             ((t0 = prof_start(s)),
-             (st = finish_launch(launch_poly_bf16(bt, tl_poly_big, h.b, h.c, true, s), 3, s, t0))))
+             (st = finish_launch(launch_poly_bf16(bt, tl_poly_big, h.a, h.b, h.c, true, s), 3, s, t0))))
           return st;
         const int fuse_tail = (it == ns_steps - 1 && any_fused) ? 1 : 0;
         const int ph = fuse_tail ? kPhaseUpdateTail : 4;
@@ -490,7 +490,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
           TileList tl = big ? tl_upd_big : tl_upd;
           if (!tl.ngroups) continue;
           tl.fuse_tail = fuse_tail;
-          if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, h.a, big != 0, s), ph, s, t0)))
+          if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, big != 0, s), ph, s, t0)))
             return st;
         }
       } else {

@@ -10,7 +10,8 @@
 //                                   are zero, and stay zero under the
 //                                   iteration, so the GEMM kernels need no
 //                                   edge masking.
-//   A, B    [count][p_pad][p_pad]   Gram matrix X X^T and polynomial b A + c A A
+//   A, B    [count][p_pad][p_pad]   Gram matrix X X^T and polynomial a I + b A + c A A
+//                                   (bf16 path; b A + c A A on the fp32 path)
 //   head    [count][head_tiles]     per-tile partial sums of u^2
 //   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
 //   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
@@ -279,10 +280,11 @@ hipError_t launch_tail_apply(const Batch& bt, const Work& wk, bool bf16, const H
 // Newton-Schulz products.  `iter` selects X0/X1 and the first-iteration norm
 // scaling.
 hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s);
-hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float b, float c, bool big,
+// The bf16 polynomial stores B = a*I + b*A + c*A*A, so that the bf16 update
+// is the plain product X' = B X.
+hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float a, float b, float c, bool big,
                             hipStream_t s);
-hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, float a, bool big,
-                              hipStream_t s);
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s);
 hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s);
 hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
 hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);

@@ -53,8 +53,8 @@ def test_fp32_256x512(variant, wd):
     e, _, ost = check_against_oracle(W, G, M, W1, M1, variant=variant, stats=st, weight_decay=wd)
     print(f"fp32 256x512 {variant} wd={wd}: relF(dW) = {e:.2e}")
     if variant == "muongs":
-        ratio = check_muongs_invariants(W, W1, 0.02, wd, cos_tol=1e-6, r2_tol=1e-6)
-        assert ratio <= 1.0  # ||O~|| <= sqrt(p) on these inputs
+        # ||O~|| <= sqrt(p) on these inputs (asserted inside)
+        check_muongs_invariants(W, W1, 0.02, wd, cos_tol=1e-6, r2_tol=1e-6)
 
 
 # -------------------------------------------- ragged shapes, whole matrices
@@ -129,34 +129,32 @@ def test_bf16_large_tiles(variant, stats):
 # Plain Muon without statistics: on the bf16 path the last Newton-Schulz
 # update applies the step to W itself whenever the weight's row length is a
 # multiple of 8 (the other shapes here take the separate tail).
+# (An 8x8 square matrix is not among them: with p = 8 the smallest singular
+# directions carry much of the update, the iteration multiplies
+# perturbations there by up to a^5 = 487, and X0's bf16 storage alone then
+# exceeds the 3e-2 bar on some inputs — 2 of 40 seeds in an fp64 emulation
+# of the bf16 path.  16x16, 8x64 and 64x8 keep the smallest shapes covered.)
 FUSED_SHAPES = [(256, 512), (512, 256), (200, 304), (304, 200), (1000, 64), (64, 1000),
-                (257, 129), (129, 257), (8, 8), (384, 384)]
+                (257, 129), (129, 257), (16, 16), (8, 64), (64, 8), (384, 384)]
 
 
 @pytest.mark.parametrize("shape", FUSED_SHAPES)
 @pytest.mark.parametrize("ns", [1, 5])
 def test_bf16_without_stats(shape, ns):
-    """The step applied by the last update (no statistics) against the oracle
-    and against the separate tail (statistics requested) on the same inputs.
-    One iteration leaves ||O|| near 3.4 instead of near sqrt(p): the bf16
-    update is then a few bf16 spacings of W, so the bar adds what rounding
-    the exact W' to bf16 costs.  On an 8x8 matrix the relative error of 64
-    elements can exceed the bar on both paths alike: there the fused result
-    must be no worse than the separate one."""
+    """The step applied by the last update (no statistics) and the separate
+    tail (statistics requested) on the same inputs, each against the oracle.
+    The bar is the bf16 tolerance plus what rounding the exact W' to bf16
+    costs on its own (relative to the update): one iteration leaves ||O||
+    near 3.4 instead of near sqrt(p), and the update of a 16x16 matrix is a
+    few bf16 spacings of W, so there the final rounding is a visible share of
+    the error on both paths."""
     W, G, M = inputs(*shape, torch.bfloat16, seed=hash(shape) % 10000 + ns, m_std=1e-3)
     W1, M1, _ = gpu_step(W, G, M, stats=False, ns_steps=ns)
-    W2, M2, _ = gpu_step(W, G, M, stats=True, ns_steps=ns)
+    W2, M2, st = gpu_step(W, G, M, stats=True, ns_steps=ns)
     assert torch.equal(M1, M2)
-    Wr, Mr, _ = oracle_step(W, G, M, ns_steps=ns)
-    w0 = f64(W)
-    e_f = relF(f64(W1) - w0, Wr - w0)
-    e_s = relF(f64(W2) - w0, Wr - w0)
-    tol = TOL_BF16
-    if ns == 1:
-        tol += relF(bf16_round(Wr), Wr) * float(np.linalg.norm(Wr) / np.linalg.norm(Wr - w0))
+    e_f, _, _ = check_against_oracle(W, G, M, W1, M1, ns_steps=ns, rounding_floor=True)
+    e_s, _, _ = check_against_oracle(W, G, M, W2, M2, ns_steps=ns, rounding_floor=True, stats=st)
     print(f"bf16 {shape} ns={ns}: relF(dW) fused {e_f:.2e}, separate tail {e_s:.2e}")
-    assert e_f <= tol or (min(shape) < 32 and e_f <= 1.1 * e_s), (e_f, e_s, tol)
-    assert relF(f64(M1), Mr) <= TOL_M
 
 
 def test_fused_and_separate_tail_agree():
@@ -363,60 +361,128 @@ def run_workload(w, step, Ws, Ms, variant, stats=None):
 
 
 def sampled(w, per_group=2):
+    """The first, a middle and the last matrix of every group (per_group >= 2),
+    or the first and a middle one."""
     out = []
     for gi, g in enumerate(w.groups):
-        idx = sorted({0, g.count - 1} if per_group >= 2 else {0})
-        out += [(gi, i) for i in idx]
+        idx = {0, g.count // 2} | ({g.count - 1} if per_group >= 2 else set())
+        out += [(gi, i) for i in sorted(idx)]
     return out
+
+
+def slice_boundary_matrices(w):
+    """The matrices next to a boundary between the eight XCD slices of any
+    Newton-Schulz launch of a grouped call over the workload.  Each launch
+    gives XCD x the contiguous tiles [n x / 8, n (x + 1) / 8) of a group's
+    n = count x tiles-per-matrix tiles; the tiles per matrix are those of the
+    128-wide symmetric tiles ((p_pad/128)(p_pad/128 + 1)/2) and update tiles
+    ((p_pad/128)(q_pad/256)), and, for matrices that may take them, of the
+    256x256 ones.  For every boundary b the matrices holding tiles b - 1 and
+    b are returned (one matrix when b falls inside it)."""
+    out = set()
+    for gi, g in enumerate(w.groups):
+        p, q = min(g.rows, g.cols), max(g.rows, g.cols)
+        pp, qp = -(-p // 128) * 128, -(-q // 256) * 256
+        nt = pp // 128
+        per = {nt * (nt + 1) // 2, nt * (qp // 256)}
+        if p >= 512 and pp % 256 == 0 and qp % 256 == 0:
+            nb = pp // 256
+            per |= {nb * (nb + 1) // 2, nb * (qp // 256)}
+        for tiles in per:
+            n = g.count * tiles
+            for x in range(1, 8):
+                b = n * x // 8
+                out |= {(gi, (b - 1) // tiles), (gi, b // tiles)}
+    return sorted(k for k in out if 0 <= k[1] < w.groups[k[0]].count)
+
+
+def graded_matrices(w):
+    return sorted(set(sampled(w)) | set(slice_boundary_matrices(w)))
 
 
 @pytest.mark.parametrize("variant,with_stats", [("muon", True), ("muongs", True), ("muon", False)])
 def test_gpt160m_full_set(variant, with_stats):
     """The grouped launch the benchmark times (without statistics: the step
-    is applied by the last update), and with per-matrix statistics."""
+    is applied by the last update), and with per-matrix statistics; graded
+    on the first, middle and last matrix of every group and on every matrix
+    next to an XCD slice boundary of the launches."""
     w = wl.WORKLOADS["gpt160m"]
     Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
     stats = torch.zeros(w.n_matrices * 5, device=DEV) if with_stats else None
     W0, Gs, M0 = run_workload(w, 0, Ws, Ms, variant, stats)
     base = np.cumsum([0] + [g.count for g in w.groups])
-    for gi, i in sampled(w):
+    picks = graded_matrices(w)
+    worst = 0.0
+    for gi, i in picks:
         st = stats[(base[gi] + i) * 5:(base[gi] + i + 1) * 5] if with_stats else None
         e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i], Ms[gi][i],
                                        variant=variant, stats=st)
-        print(f"gpt160m {w.groups[gi]} #{i} {variant}: relF(dW) = {e:.2e}")
+        worst = max(worst, e)
         if variant == "muongs":
-            check_muongs_invariants(W0[gi][i], Ws[gi][i], 0.02, 0.1, cos_tol=1e-3, r2_tol=1e-3)
+            check_muongs_invariants(W0[gi][i], Ws[gi][i], 0.02, 0.1, cos_tol=1e-3, r2_tol=1e-3,
+                                    ratio_max=1.01)
+    print(f"gpt160m {variant}: {len(picks)} of {w.n_matrices} matrices graded, "
+          f"worst relF(dW) = {worst:.2e}")
 
 
 def test_gpt400m_consecutive_steps():
     """Ten consecutive Muon and MuonGS steps with a fresh gradient every step
-    (the GPT-400M configuration); steps 0, 4 and 9 graded against the oracle
-    from the GPU's own W_t, M_t (teacher forcing), with the MuonGS invariants
-    on those steps; every step leaves W and M finite."""
+    (the GPT-400M configuration).  Graded against the oracle from the GPU's
+    own W_t, M_t (teacher forcing): step 0 on the first, middle and last
+    matrix of every group and every matrix next to an XCD slice boundary,
+    steps 4 and 9 on the first and a middle matrix of every group, with the
+    MuonGS invariants on those matrices; every step leaves W and M finite.
+    The free-running drift (the oracle's own ten steps in fp64 from the same
+    start, against the GPU's ten) is reported, not graded."""
     w = wl.WORKLOADS["gpt400m"]
+    drift_picks = sampled(w, per_group=1)
     for variant in ("muon", "muongs"):
         Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
+        free = {k: (f64(Ws[k[0]][k[1]]), f64(Ms[k[0]][k[1]])) for k in drift_picks}
+        start = {k: v[0].copy() for k, v in free.items()}
+        worst = 0.0
         for step in range(10):
             W0, Gs, M0 = run_workload(w, step, Ws, Ms, variant)
             assert all(bool(torch.isfinite(x).all()) for x in Ws + Ms), step
-            if step not in (0, 4, 9):
+            for k in drift_picks:
+                Wf, Mf, _ = oracle.muon_step(free[k][0], f64(Gs[k[0]][k[1]]), free[k][1],
+                                             variant=variant, **HP)
+                free[k] = (Wf, Mf)
+            if step == 0:
+                picks = graded_matrices(w)
+            elif step in (4, 9):
+                picks = sampled(w, per_group=1)
+            else:
                 continue
-            for gi, i in sampled(w, per_group=1):
+            for gi, i in picks:
                 e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i],
                                                Ms[gi][i], variant=variant)
+                worst = max(worst, e)
                 if variant == "muongs":
                     check_muongs_invariants(W0[gi][i], Ws[gi][i], 0.02, 0.1, cos_tol=1e-3,
-                                            r2_tol=1e-3)
-                print(f"gpt400m step {step} {w.groups[gi]} {variant}: relF(dW) = {e:.2e}")
+                                            r2_tol=1e-3, ratio_max=1.01)
+            print(f"gpt400m step {step} {variant}: {len(picks)} matrices graded, "
+                  f"worst relF(dW) = {worst:.2e}", flush=True)
+        for gi, i in drift_picks:
+            w10, w0 = f64(Ws[gi][i]), start[(gi, i)]
+            d = relF(w10 - w0, free[(gi, i)][0] - w0)
+            print(f"gpt400m {variant} {w.groups[gi]} #{i}: free-running 10-step drift "
+                  f"relF(W_10 - W_0) = {d:.2e} (reported, not graded)")
 
 
 def test_moe_full_set():
+    """The whole MoE-1B set (4288 matrices) in one grouped call, graded on the
+    first, middle and last matrix of every group and every matrix next to an
+    XCD slice boundary of its launches."""
     w = wl.WORKLOADS["moe1b"]
     Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
     W0, Gs, M0 = run_workload(w, 0, Ws, Ms, "muon")
-    for gi, i in sampled(w):
+    picks = graded_matrices(w)
+    worst = 0.0
+    for gi, i in picks:
         e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i], Ms[gi][i])
-        print(f"moe1b {w.groups[gi]} #{i}: relF(dW) = {e:.2e}")
+        worst = max(worst, e)
+    print(f"moe1b: {len(picks)} of {w.n_matrices} matrices graded, worst relF(dW) = {worst:.2e}")
 
 
 def test_stress_matrices_sampled():
@@ -583,3 +649,151 @@ def test_equalisation_gpt160m_grouped(variant):
         assert relF(f64(Ms[gi][i]), Mr) <= TOL_M
         print(f"gpt160m {w.groups[gi]} #{i} {variant}: spreads {sr:.4f}/{sc:.4f}, "
               f"{'rows' if gpu_rows else 'cols'}, relF(dW) = {e:.2e}")
+
+
+# ------------------------------------------- launch sequences and front end
+# Eleven shape groups: more than the eight one launch sequence takes, so the
+# call runs two sequences (the second with its own workspace regions and
+# statistics offset); three row lengths are not multiples of 8, so without
+# statistics those groups take the separate tail while the others have the
+# step applied by their last update, in the same launches.
+MANY_GROUPS = [(3, 64, 96), (2, 96, 64), (4, 128, 128), (2, 100, 130), (3, 130, 100),
+               (2, 256, 72), (1, 72, 256), (2, 33, 257), (2, 200, 304), (1, 384, 128),
+               (2, 48, 48)]
+
+
+@pytest.mark.parametrize("variant,with_stats", [("muon", False), ("muon", True), ("muongs", True)])
+def test_more_groups_than_one_launch_sequence(variant, with_stats):
+    Ws = [wl.random_matrix(c * r, k, 0.02, 1300 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(MANY_GROUPS)]
+    Gs = [wl.random_matrix(c * r, k, 1e-3, 1400 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(MANY_GROUPS)]
+    Ms = [wl.random_matrix(c * r, k, 1e-3, 1500 + i, torch.float32, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(MANY_GROUPS)]
+    W0 = [w.clone() for w in Ws]
+    M0 = [m.clone() for m in Ms]
+    total = sum(c for c, _, _ in MANY_GROUPS)
+    st = torch.full((total * 5,), float("nan"), device=DEV) if with_stats else None
+    muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Ws, Gs, Ms)], torch.bfloat16,
+                      variant=variant, stats=st, **HP)
+    torch.cuda.synchronize()
+    if with_stats:
+        assert bool(torch.isfinite(st).all())   # every matrix's row written
+    k = 0
+    for gi, (c, r, cols) in enumerate(MANY_GROUPS):
+        for i in range(c):
+            s5 = st[5 * k:5 * k + 5] if with_stats else None
+            e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i], Ms[gi][i],
+                                           variant=variant, stats=s5, rounding_floor=min(r, cols) < 64)
+            k += 1
+        print(f"group {gi} {r}x{cols} {variant} stats={with_stats}: relF(dW) = {e:.2e}")
+
+
+def test_side_stream_matches_default_stream():
+    """A call on a stream other than the current one, with allocations on the
+    current stream made before anything is synchronised: the binding's own
+    workspace must not be handed out again while the kernels still use it,
+    so the result is bitwise that of the same call on the current stream."""
+    w = wl.WORKLOADS["gpt160m"]
+    Gs = wl.make_grads(w, 0, DEV)
+    Wa, Ma = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
+    Wb, Mb = [x.clone() for x in Wa], [x.clone() for x in Ma]
+    torch.cuda.synchronize()
+    muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Wa, Gs, Ma)], torch.bfloat16,
+                      **HP)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Wb, Gs, Mb)], torch.bfloat16,
+                      stream=side, **HP)
+    # the current stream allocates and writes while the side stream still runs
+    junk = [torch.full((1 << 26,), 7, dtype=torch.uint8, device=DEV) for _ in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    for x, y in zip(Wa + Ma, Wb + Mb):
+        assert torch.equal(x, y)
+
+
+def test_checkpoint_split_run_is_bitwise():
+    """The optimizer state is the momentum buffer alone (one per matrix): k
+    steps, W and M copied to the host and restored into fresh tensors (and a
+    fresh workspace), then the remaining steps, give bitwise the weights and
+    momenta of an uninterrupted run."""
+    shapes = [(4, 256, 640), (2, 640, 256), (3, 200, 130)]
+    def fresh():
+        return ([wl.random_matrix(c * r, k, 0.02, 1600 + i, torch.bfloat16, DEV).view(c, r, k)
+                 for i, (c, r, k) in enumerate(shapes)],
+                [torch.zeros(c, r, k, device=DEV) for c, r, k in shapes])
+    def grads(step):
+        return [wl.random_matrix(c * r, k, 1e-3, 1700 + 10 * step + i, torch.bfloat16, DEV)
+                .view(c, r, k) for i, (c, r, k) in enumerate(shapes)]
+    def run(Ws, Ms, steps):
+        for t in steps:
+            Gs = grads(t)
+            muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Ws, Gs, Ms)],
+                              torch.bfloat16, **HP)
+        torch.cuda.synchronize()
+    Wa, Ma = fresh()
+    run(Wa, Ma, range(6))
+    Wb, Mb = fresh()
+    run(Wb, Mb, range(3))
+    saved = [(W.cpu(), M.cpu()) for W, M in zip(Wb, Mb)]
+    del Wb, Mb
+    torch.cuda.empty_cache()
+    Wc = [W.to(DEV) for W, _ in saved]
+    Mc = [M.to(DEV) for _, M in saved]
+    run(Wc, Mc, range(3, 6))
+    for x, y in zip(Wa + Ma, Wc + Mc):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("k", [0.125, 8.0])
+def test_gradient_scale_invariance(dtype, k):
+    """Scaling G and M by k > 0 scales U by k and leaves O, hence W', unchanged
+    up to the 1e-7 in the normaliser; M' scales by k exactly.  With k a power
+    of two every stored value scales exactly, and what remains is the
+    rounding of 1/(k ||U|| + eps) against 1/(||U|| + eps) / k (about 1e-6
+    relative here, where ||U|| = 0.53).  The iteration multiplies such a
+    perturbation along the smallest singular directions by up to a^5 = 487,
+    so in fp32 the two updates agree to the fp32 parity bar (measured
+    2.6e-6).  In bf16 the same perturbation flips a few dozen roundings of
+    the first A, and from there the two rounding sequences part: the two
+    updates then differ about as much as either differs from the oracle
+    (measured 1.07e-2), so in bf16 each is held to the oracle's bar on its
+    own inputs and their difference to that bar."""
+    W, G, M = inputs(192, 320, dtype, seed=61, m_std=1e-3)
+    W1, M1, _ = gpu_step(W, G, M, stats=False)
+    Gk = (G.float() * k).to(dtype)
+    Wk, Mk, _ = gpu_step(W, Gk, M * k, stats=False)
+    d1, dk = f64(W1) - f64(W), f64(Wk) - f64(W)
+    e = relF(dk, d1)
+    print(f"{dtype} k={k}: relF(dW_k, dW_1) = {e:.2e}")
+    assert e <= (TOL_F32 if dtype == torch.float32 else TOL_BF16)
+    assert torch.equal(Mk, M1 * k)
+    check_against_oracle(W, Gk, M * k, Wk, Mk)
+
+
+def test_optimizer_front_end_stats_and_rebinding():
+    """MuonStep over two dtypes: each dtype's call writes its own rows of the
+    statistics buffer (in stats_order), and a parameter whose .data is
+    rebound between steps is updated in its new storage."""
+    shapes = [((256, 512), torch.bfloat16), ((128, 96), torch.float32),
+              ((512, 256), torch.bfloat16), ((128, 96), torch.float32)]
+    params = [torch.nn.Parameter(wl.random_matrix(*s, 0.02, 1800 + i, dt, DEV))
+              for i, (s, dt) in enumerate(shapes)]
+    opt = MuonStep(params, variant="muongs")
+    assert sorted(opt.stats_order) == list(range(len(params)))
+    for step in range(2):
+        if step == 1:
+            params[2].data = params[2].data.clone()     # new storage
+        W0 = [p.detach().clone() for p in params]
+        M0 = [m.clone() for m in opt.momentum_buffers]
+        for i, p in enumerate(params):
+            p.grad = wl.random_matrix(*shapes[i][0], 1e-3, 1900 + 10 * step + i, shapes[i][1], DEV)
+        stats = torch.full((len(params) * 5,), float("nan"), device=DEV)
+        opt.step(stats=stats)
+        torch.cuda.synchronize()
+        for row, i in enumerate(opt.stats_order):
+            check_against_oracle(W0[i], params[i].grad, M0[i], params[i].detach(),
+                                 opt.momentum_buffers[i], variant="muongs",
+                                 stats=stats[5 * row:5 * row + 5])

@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Muon optimizer step benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt160m]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload moe1b]
 
-A step is one whole Muon step over every hidden 2-D matrix of the workload:
+A step is one whole Muon step over every hidden 2-D matrix of the workload
+(by default the MoE model with 1B parameters in total: 4288 matrices, 3.03 G
+elements, the largest full model of the workloads):
 momentum/Nesterov head, 5 Newton-Schulz iterations, scale/decay/update tail,
 issued as ONE grouped launch sequence (muon_step_grouped) on inputs already
 resident in HBM (the 2k-hidden stress set, whose whole-model workspace would
@@ -23,6 +25,10 @@ steps run up to 20 % slower while its clocks ramp up.  Prints one JSON line:
   aux_adamw   the other half of the hybrid optimizer, timed separately (not
               part of `value`): one grouped AdamW call over the model's
               embedding, head and gains, its GB/s against HBM peak
+  workloads   the other workloads, each timed the same way after the main
+              one in the same run (not part of `value`): GPT-160M, GPT-400M
+              (Muon and MuonGS), the 2k-hidden stress set (fewer steps) and
+              the single fp32 256x512 matrix (latency)
 """
 from __future__ import annotations
 
@@ -48,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps (default: as many as take 0.25 s, at least 3: "
                          "the GPU's clocks ramp up over the first tens of milliseconds)")
-    ap.add_argument("--workload", default="gpt160m")
+    ap.add_argument("--workload", default="moe1b")
     ap.add_argument("--variant", default="muon", choices=["muon", "muongs", "muonh", "normuon", "meqmuon"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
@@ -58,6 +64,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-profile", action="store_true")
     ap.add_argument("--no-aux", action="store_true", help="skip the AdamW-side measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only --workload (not the other workloads after it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -65,7 +73,8 @@ def parse():
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_update_gpt160m_hbm_traffic.md")
+# Committed counter summaries, one per workload: profiles/ns_update_<workload>_hbm_traffic.md
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_update_{}_hbm_traffic.md")
 # The sources the update kernel is built from: traffic counters are only
 # reported while these are unchanged since the counters were taken.
 KERNEL_SOURCES = ("muon_step_03_amd/csrc/k_ns_bf16.hip", "muon_step_03_amd/csrc/muon_internal.h")
@@ -84,10 +93,11 @@ def kernel_source_hash():
 def measured_traffic(workload):
     """HBM bytes per update launch from the committed counter summary, or
     None if there is none for this workload or the kernel has changed."""
-    if workload != "gpt160m" or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
     fields = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and line.split(":", 1)[0].strip() in (
                     "traffic_bytes_per_launch", "kernel_source_sha256"):
@@ -130,11 +140,12 @@ def matrix_work(groups, dtype_bytes):
                 tail_bytes=elems * (es + es + es))      # W r, O r, W w
 
 
-def cpu_baseline(wl_mod, w, seconds):
-    """The oracle, untuned, on whole matrices drawn in layer order until about
-    `seconds` of CPU time, extrapolated to the full matrix count."""
+def cpu_baseline(w, Ws, Gs, Ms, seconds):
+    """The oracle, untuned, on the workload's own inputs (copied from the
+    device before the GPU's first step), one whole matrix at a time in layer
+    order (round-robin over the shape groups) until about `seconds` of CPU
+    time, extrapolated per shape to the full matrix count."""
     import numpy as np
-    import torch
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -144,9 +155,6 @@ def cpu_baseline(wl_mod, w, seconds):
         threads = 1
     per_shape = {}
     order = []
-    # one matrix of each group per "layer", round-robin; values are seeded
-    # Gaussians of the workload's distributions (the oracle's cost depends on
-    # the shapes only)
     for k in range(max(g.count for g in w.groups)):
         for gi, g in enumerate(w.groups):
             if k < g.count:
@@ -156,12 +164,9 @@ def cpu_baseline(wl_mod, w, seconds):
     # cycle over the model until about `seconds` (at most 4 passes)
     for gi, k in order * 4:
         g = w.groups[gi]
-        gen = torch.Generator().manual_seed(10_000 + 131 * gi + k)
-        W = (torch.randn(g.rows, g.cols, generator=gen) * 0.02).to(wl_mod.torch_dtype(w.dtype))
-        G = (torch.randn(g.rows, g.cols, generator=gen) * 1e-3).to(wl_mod.torch_dtype(w.dtype))
-        Wd = W.double().numpy()
-        Gd = G.double().numpy()
-        Md = np.zeros_like(Wd)
+        Wd = Ws[gi][k].double().cpu().numpy()
+        Gd = Gs[gi][k].double().cpu().numpy()
+        Md = Ms[gi][k].double().cpu().numpy()
         t0 = time.perf_counter()
         oracle.muon_step(Wd, Gd, Md, **HP)
         dt = time.perf_counter() - t0
@@ -179,8 +184,8 @@ def cpu_baseline(wl_mod, w, seconds):
     except OSError:  # pragma: no cover
         pass
     return {"value": 1.0 / total, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} matrix steps over the {w.n_matrices} matrices (round-robin over the "
-                      f"shape groups, repeated up to 4 times), {spent:.1f} s of fp64 NumPy; "
+            "sample": f"{done} matrix steps over the {w.n_matrices} matrices (the GPU's own "
+                      f"inputs, round-robin over the shape groups), {spent:.1f} s of fp64 NumPy; "
                       f"seconds/step = per-shape mean x count",
             "seconds_per_step": total, "host_cpus": os.cpu_count(), "cpu_model": model}
 
@@ -232,6 +237,200 @@ def aux_adamw(args, wl, dev, stream, muon_ms):
             "hyper": {"betas": [0.8, 0.95], "eps": 1e-10, "weight_decay": 1e-3, "lr": AUX_LR}}
 
 
+def phase_profile(L, step, steps, w, es):
+    """Per-launch kernel times (HIP events on the launch stream, recorded by
+    the library around every launch) over `steps` more steps: the roofline
+    of the update launch, the Newton-Schulz phase and the head/tail GB/s."""
+    from muon_step_03_amd import _lib
+    import torch
+    L.muon_profile_enable(1)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    L.muon_profile_enable(0)
+    n = _lib.MUON_NUM_PHASES
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    assert L.muon_profile_read(ms, cnt, n) == 0
+    names = [L.muon_phase_name(i).decode() for i in range(n)]
+    avg = {names[i]: (ms[i] / cnt[i] if cnt[i] else 0.0) for i in range(n)}
+    per_step = {names[i]: ms[i] / steps for i in range(n)}
+    per = {names[i]: cnt[i] / steps for i in range(n)}
+    work = matrix_work(w.groups, es)
+    peak = PEAK_MFMA[w.dtype]
+    out = {}
+    # Algorithmic flops per "update" launch: the update work of every
+    # iteration timed in this phase (the last one is timed apart when it
+    # also applies the step), spread over its launches (two per iteration
+    # when a phase runs both tile sizes, more when the model is split over
+    # several calls).
+    upd_iters = HP["ns_steps"] - (1 if per["update_tail"] > 0 else 0)
+    if per["update"] > 0:
+        upd_flops = work["update"] * upd_iters / per["update"]
+        a = upd_flops / (avg["update"] * 1e-3)
+        out["roofline"] = {
+            "kernel": "ns_update (X' = BX, B = aI + bA + cA^2)" if w.dtype == "bf16"
+                      else "ns_update (X' = aX + BX)",
+            "bound": "mfma", "achieved": a / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+            "frac": a / peak, "traffic": measured_traffic(w.name), "avg_launch_ms": avg["update"],
+            "alg_flops_per_launch": upd_flops,
+        }
+        # The same launch against the HBM roofline: its algorithmic bytes
+        # (B and X read once, X' written once, unpadded shapes) over the same
+        # time, and the arithmetic intensity against the ridge point (dense
+        # peak / HBM peak).
+        upd_bytes = work["update_bytes"] * upd_iters / per["update"]
+        out["roofline"]["hbm_view"] = {
+            "alg_bytes_per_launch": upd_bytes,
+            "gbps": upd_bytes / (avg["update"] * 1e-3) / 1e9,
+            "frac_of_hbm": upd_bytes / (avg["update"] * 1e-3) / PEAK_HBM,
+            "flop_per_byte": upd_flops / upd_bytes, "ridge_flop_per_byte": peak / PEAK_HBM,
+        }
+    ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"] + per_step["update_tail"]
+    ns_flops = HP["ns_steps"] * (work["gram"] + work["poly"] + work["update"])
+    out["ns"] = {"ms_per_step": ns_ms, "tflops": ns_flops / (ns_ms * 1e-3) / 1e12,
+                 "frac_of_peak": ns_flops / (ns_ms * 1e-3) / peak,
+                 "alg_tflop_per_step": ns_flops / 1e12,
+                 "avg_launch_ms": {k: avg[k] for k in ("gram", "poly", "update")}}
+    if per_step["update_tail"] > 0:
+        out["ns"]["last_update_with_step_ms"] = avg["update_tail"]
+    # per step: a model split over several calls has one head launch per call
+    out["head"] = {"ms": per_step["head"],
+                   "gbps": work["head_bytes"] / (per_step["head"] * 1e-3) / 1e9,
+                   "frac_of_hbm": work["head_bytes"] / (per_step["head"] * 1e-3) / PEAK_HBM}
+    tail_ms = per_step["tail_apply"] + per_step["tail_reduce"] + per_step["tail_finalize"]
+    if tail_ms > 0:
+        out["tail"] = {"ms": tail_ms, "gbps": work["tail_bytes"] / (tail_ms * 1e-3) / 1e9,
+                       "frac_of_hbm": work["tail_bytes"] / (tail_ms * 1e-3) / PEAK_HBM}
+    else:
+        out["tail"] = {"ms": 0.0, "fused_into_last_update": True}
+    out["phase_ms_per_step"] = per_step
+    return out
+
+
+def measure(name, variant, steps, warmup, args, cpu_seconds=None, main=False):
+    """Times exactly `steps` whole steps of workload `name` (after `warmup`
+    untimed ones, or 0.25 s of them when None), then the same number again
+    with one event pair per step, then the phase profile.  Inputs are drawn
+    on the device and stay resident; they are freed on return."""
+    import torch
+    from muon_step_03_amd import _lib, muon_step_grouped, stacked_chunks
+    from muon_step_03_amd import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    tdtype = wl.torch_dtype(w.dtype)
+    es = 2 if w.dtype == wl.BF16 else 4
+    torch.cuda.empty_cache()
+    Ws = wl.make_weights(w, dev)
+    Gs = wl.make_grads(w, 0, dev)
+    Ms = wl.make_momentum(w, dev)
+    torch.cuda.empty_cache()   # the generators' float32 temporaries
+    out = {}
+    if cpu_seconds:
+        # the oracle on the GPU's own inputs, before the first GPU step
+        out["cpu_baseline"] = cpu_baseline(w, Ws, Gs, Ms, cpu_seconds)
+    # One grouped call over the whole model when its workspace fits the
+    # budget (every workload but the 2k-hidden stress set), else the fewest
+    # calls over even chunks of every group.
+    calls, ws_bytes = stacked_chunks(zip(Ws, Gs, Ms), tdtype, int(args.max_workspace_gb * 2**30))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    hp = dict(HP, ns_coefficients=NS_COEFFS, variant=variant)
+
+    def step():
+        for groups in calls:
+            muon_step_grouped(groups, tdtype, workspace=ws, device=dev, stream=stream, **hp)
+
+    if warmup is None:
+        # by time: at least 3 steps and 0.25 s of work
+        torch.cuda.synchronize()
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 3 or time.perf_counter() - t_w < 0.25:
+            step()
+            n_w += 1
+            if n_w % 8 == 0:
+                torch.cuda.synchronize()
+        warmup = n_w
+    else:
+        for _ in range(warmup):
+            step()
+    torch.cuda.synchronize()
+    print(f"# {name} {variant}: warmup done ({warmup} steps)", file=sys.stderr, flush=True)
+
+    # ---- timed region: exactly `steps` steps, synchronised on both sides
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ev_ms = start.elapsed_time(stop)
+    ms_per_step = max(ev_ms, wall_ms) / steps
+    print(f"# {name} {variant}: timed {steps} steps: {ms_per_step:.4f} ms/step",
+          file=sys.stderr, flush=True)
+
+    # ---- per-step distribution: the same number of steps again, one event pair each
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    def pct(q):
+        return per_step_ms[min(len(per_step_ms) - 1, int(q * (len(per_step_ms) - 1) + 0.5))]
+
+    out.update({
+        "value": 1e3 / ms_per_step, "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup,
+        "dtype": w.dtype,
+        "config": {"workload": w.name, "description": w.description, "matrices": w.n_matrices,
+                   "elements": w.n_elements, "variant": variant, "ns_steps": HP["ns_steps"],
+                   "lr": HP["lr"], "momentum": HP["momentum"],
+                   "weight_decay": HP["weight_decay"],
+                   "launch": ("muon_step_grouped, one launch sequence per step" if len(calls) == 1
+                              else f"muon_step_grouped, {len(calls)} calls per step over "
+                                   f"chunks of {calls[0][0].count} matrices per shape"),
+                   "workspace_bytes": ws_bytes},
+        "step_ms": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
+                    "note": "a second pass of the same number of steps, one event pair per step"},
+    })
+    if not args.no_phase_profile:
+        out.update(phase_profile(_lib.lib(), step, steps, w, es))
+    if main and not args.no_aux and name in wl.AUX_SETS:
+        out["aux_adamw"] = aux_adamw(args, wl, dev, stream, ms_per_step)
+    del Ws, Gs, Ms, ws, calls
+    torch.cuda.empty_cache()
+    return out
+
+
+# The other workloads timed after the main one: (name, variant, steps, warmup);
+# None takes --steps / --warmup.  The stress set moves 189 GB of W, G and M per
+# step (about a second): two timed steps after one warm-up.
+EXTRAS = (("gpt160m", "muon", None, None), ("gpt400m", "muon", None, None),
+          ("gpt400m", "muongs", None, None), ("moe1b", "muongs", None, None),
+          ("stress2k", "muon", 2, 1), ("fp32_256x512", "muon", None, None))
+
+
+def summary(r):
+    """The figures of one extra workload kept in the JSON line."""
+    keys = ("value", "ms_per_step", "steps", "warmup", "dtype", "config", "step_ms")
+    out = {k: r[k] for k in keys if k in r}
+    out["unit"] = "steps/s"
+    if "roofline" in r:
+        out["roofline_update"] = {k: r["roofline"][k] for k in
+                                  ("achieved", "frac", "avg_launch_ms", "traffic")}
+    for k in ("ns", "head", "tail", "phase_ms_per_step"):
+        if k in r:
+            out[k] = r[k]
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -245,161 +444,30 @@ def main():
         return
 
     import torch
-    from muon_step_03_amd import _lib, muon_step_grouped, stacked_chunks
     from muon_step_03_amd import workloads as wl
 
+    torch.cuda.set_device(torch.device("cuda", 0))
     w = wl.WORKLOADS[args.workload]
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    tdtype = wl.torch_dtype(w.dtype)
-    es = 2 if w.dtype == wl.BF16 else 4
-
-    Ws = wl.make_weights(w, dev)
-    Gs = wl.make_grads(w, 0, dev)
-    Ms = wl.make_momentum(w, dev)
-    torch.cuda.empty_cache()   # the generators' float32 temporaries
-    # One grouped call over the whole model when its workspace fits the
-    # budget (every workload but the 2k-hidden stress set), else the fewest
-    # calls over even chunks of every group.
-    calls, ws_bytes = stacked_chunks(zip(Ws, Gs, Ms), tdtype, int(args.max_workspace_gb * 2**30))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    hp = dict(HP, ns_coefficients=NS_COEFFS, variant=args.variant)
-
-    def step():
-        for groups in calls:
-            muon_step_grouped(groups, tdtype, workspace=ws, device=dev, stream=stream, **hp)
-
-    if args.warmup is None:
-        # by time: at least 3 steps and 0.25 s of work
-        torch.cuda.synchronize()
-        t_w, n_w = time.perf_counter(), 0
-        while n_w < 3 or time.perf_counter() - t_w < 0.25:
-            step()
-            n_w += 1
-            if n_w % 8 == 0:
-                torch.cuda.synchronize()
-        args.warmup = n_w
-    else:
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    # ---- timed region: exactly K steps, synchronised on both sides
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    ev_ms = start.elapsed_time(stop)
-    ms_per_step = max(ev_ms, wall_ms) / args.steps
-    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
-
-    # ---- per-step distribution: the same K steps again, one event pair each
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    per_step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-
-    def pct(q):
-        return per_step_ms[min(len(per_step_ms) - 1, int(q * (len(per_step_ms) - 1) + 0.5))]
-
-    work = matrix_work(w.groups, es)
+    main_r = measure(args.workload, args.variant, args.steps, args.warmup, args,
+                     cpu_seconds=None if args.no_cpu_baseline else args.cpu_seconds, main=True)
     result = {
-        "metric": METRIC, "value": 1e3 / ms_per_step, "unit": "steps/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "metric": METRIC, "value": main_r["value"], "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": main_r["warmup"], "ms_per_step": main_r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian W ~ N(0, 0.02^2), G ~ N(0, 1e-3^2), M = 0)",
-        "config": {"workload": w.name, "description": w.description, "matrices": w.n_matrices,
-                   "elements": w.n_elements, "variant": args.variant, "ns_steps": 5,
-                   "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1,
-                   "launch": ("muon_step_grouped, one launch sequence per step" if len(calls) == 1
-                              else f"muon_step_grouped, {len(calls)} calls per step over "
-                                   f"chunks of {calls[0][0].count} matrices per shape"),
-                   "workspace_bytes": ws_bytes},
-        "step_ms": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9),
-                    "note": "a second pass of the same number of steps, one event pair per step"},
+        "config": main_r["config"], "step_ms": main_r["step_ms"],
     }
-
-    # ---- per-launch kernel times with HIP events on the launch stream
-    if not args.no_phase_profile:
-        L = _lib.lib()
-        L.muon_profile_enable(1)
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        L.muon_profile_enable(0)
-        n = _lib.MUON_NUM_PHASES
-        ms = (ctypes.c_double * n)()
-        cnt = (ctypes.c_int64 * n)()
-        assert L.muon_profile_read(ms, cnt, n) == 0
-        avg = {L.muon_phase_name(i).decode(): (ms[i] / cnt[i] if cnt[i] else 0.0) for i in range(n)}
-        per_step = {L.muon_phase_name(i).decode(): ms[i] / args.steps for i in range(n)}
-        peak = PEAK_MFMA[w.dtype]
-        # Algorithmic flops per "update" launch: the update work of every
-        # iteration timed in this phase (the last one is timed apart when it
-        # also applies the step), spread over its launches (two per
-        # iteration when the library runs two chains).
-        per = {k: cnt[i] / args.steps for i, k in enumerate(
-            L.muon_phase_name(i).decode() for i in range(n))}
-        upd_iters = HP["ns_steps"] - (1 if per["update_tail"] > 0 else 0)
-        upd_flops = work["update"] * upd_iters / per["update"]
-        a = upd_flops / (avg["update"] * 1e-3)
-        result["roofline"] = {
-            "kernel": "ns_update (X' = aX + B X)", "bound": "mfma",
-            "achieved": a / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s", "frac": a / peak,
-            "traffic": measured_traffic(w.name), "avg_launch_ms": avg["update"],
-            "alg_flops_per_launch": upd_flops,
-        }
-        # The same launch against the HBM roofline: its algorithmic bytes
-        # (B and X read once, X' written once, unpadded shapes) over the
-        # same time, and the arithmetic intensity against the ridge point
-        # (dense bf16 peak / HBM peak = 312 flop/byte).
-        upd_bytes = work["update_bytes"] * upd_iters / per["update"]
-        result["roofline"]["hbm_view"] = {
-            "alg_bytes_per_launch": upd_bytes,
-            "gbps": upd_bytes / (avg["update"] * 1e-3) / 1e9,
-            "frac_of_hbm": upd_bytes / (avg["update"] * 1e-3) / PEAK_HBM,
-            "flop_per_byte": upd_flops / upd_bytes, "ridge_flop_per_byte": peak / PEAK_HBM,
-        }
-        # The last update of a step may also apply the step to W (plain Muon
-        # without statistics, bf16): it is timed as its own phase, so
-        # "update" stays the pure GEMM launch of the roofline.
-        ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"] + per_step["update_tail"]
-        ns_flops = 5 * (work["gram"] + work["poly"] + work["update"])
-        result["ns"] = {"ms_per_step": ns_ms, "tflops": ns_flops / (ns_ms * 1e-3) / 1e12,
-                        "frac_of_peak": ns_flops / (ns_ms * 1e-3) / peak,
-                        "alg_tflop_per_step": ns_flops / 1e12,
-                        "avg_launch_ms": {k: avg[k] for k in ("gram", "poly", "update")}}
-        # per step: a model split over several calls has one head launch per call
-        result["head"] = {"ms": per_step["head"],
-                          "gbps": work["head_bytes"] / (per_step["head"] * 1e-3) / 1e9,
-                          "frac_of_hbm": work["head_bytes"] / (per_step["head"] * 1e-3) / PEAK_HBM}
-        tail_ms = per_step["tail_apply"] + per_step["tail_reduce"] + per_step["tail_finalize"]
-        if tail_ms > 0:
-            result["tail"] = {"ms": tail_ms, "gbps": work["tail_bytes"] / (tail_ms * 1e-3) / 1e9,
-                              "frac_of_hbm": work["tail_bytes"] / (tail_ms * 1e-3) / PEAK_HBM}
-        else:
-            result["tail"] = {"ms": 0.0, "fused_into_last_update": True}
-        if per_step["update_tail"] > 0:
-            result["ns"]["last_update_with_step_ms"] = avg["update_tail"]
-        result["phase_ms_per_step"] = per_step
-
-    if not args.no_aux and args.workload in wl.AUX_SETS:
-        result["aux_adamw"] = aux_adamw(args, wl, dev, stream, ms_per_step)
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, w, args.cpu_seconds)
-
+    for k in ("roofline", "ns", "head", "tail", "phase_ms_per_step", "aux_adamw", "cpu_baseline"):
+        if k in main_r:
+            result[k] = main_r[k]
+    if not args.no_extras:
+        result["workloads"] = {}
+        for name, variant, steps, warmup in EXTRAS:
+            if (name, variant) == (args.workload, args.variant):
+                continue
+            r = measure(name, variant, steps or args.steps,
+                        warmup if steps else args.warmup, args)
+            result["workloads"][f"{name}/{variant}"] = summary(r)
     print(json.dumps(result), flush=True)
 
 

@@ -57,11 +57,28 @@ def test_matrix_work_closed_form():
 def test_traffic_figure_needs_matching_sources(tmp_path, monkeypatch):
     """The committed counter summary is used only while the kernel sources
     hash to the value recorded with it."""
-    f = tmp_path / "traffic.md"
+    f = tmp_path / "ns_update_moe1b_hbm_traffic.md"
     f.write_text("traffic_bytes_per_launch: 123456\n"
                  f"kernel_source_sha256: `{bench.kernel_source_hash()}`\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic("gpt160m") == 123456
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "ns_update_{}_hbm_traffic.md"))
+    assert bench.measured_traffic("moe1b") == 123456
     assert bench.measured_traffic("gpt400m") is None
     f.write_text("traffic_bytes_per_launch: 123456\nkernel_source_sha256: `0000`\n")
-    assert bench.measured_traffic("gpt160m") is None
+    assert bench.measured_traffic("moe1b") is None
+
+
+def test_default_workload_is_the_largest_full_model():
+    """The headline is timed on the MoE model (the largest full model of the
+    workloads), and the other workloads are listed to be timed after it."""
+    ap_args = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        args = bench.parse()
+    finally:
+        sys.argv = ap_args
+    assert args.workload == "moe1b"
+    assert max(wl.WORKLOADS[n].n_elements for n in ("gpt160m", "gpt400m", "moe1b")) == \
+        wl.WORKLOADS["moe1b"].n_elements
+    names = {(n, v) for n, v, _, _ in bench.EXTRAS}
+    assert {("gpt160m", "muon"), ("gpt400m", "muon"), ("gpt400m", "muongs"),
+            ("stress2k", "muon"), ("fp32_256x512", "muon")} <= names

@@ -623,11 +623,14 @@ def test_row_column_equalisation(dtype, shape, heavy, variant):
 def test_equalisation_gpt160m_grouped(variant):
     """The grouped launch over the 72 GPT-160M matrices (three shape groups).
     A nearly orthogonal square O has row and column spreads of about 1 % and
-    close to each other, so MeqMuon's choice can go either way between fp32
-    and fp64: the direction the GPU took is read off its output (the
-    equalised side), must be the oracle's wherever the two spreads differ by
-    more than 2 %, and the result is compared with the oracle's step for
-    that direction."""
+    close to each other, and the bf16 path's O (1.3e-2 from the oracle's)
+    moves them by a few percent of themselves, so MeqMuon's choice can go
+    either way between the bf16 path and fp64 (measured: spreads 0.0090 and
+    0.0094, 4.6 % apart, decided differently).  The direction the GPU took is
+    read off its output (the equalised side), must be the oracle's wherever
+    the two spreads differ by more than 10 % (the margin the equalisation
+    test keeps its inputs at), and the result is compared with the oracle's
+    step for that direction."""
     w = wl.WORKLOADS["gpt160m"]
     Ws, Ms = wl.make_weights(w, DEV), wl.make_momentum(w, DEV)
     W0, Gs, M0 = run_workload(w, 0, Ws, Ms, variant)
@@ -639,7 +642,7 @@ def test_equalisation_gpt160m_grouped(variant):
         rn, cn = np.linalg.norm(On, axis=1), np.linalg.norm(On, axis=0)
         gpu_rows = np.std(rn) / np.mean(rn) <= np.std(cn) / np.mean(cn)
         sr, sc = spreads(O)
-        if variant == "normuon" or abs(sr - sc) > 2e-2 * max(sr, sc):
+        if variant == "normuon" or abs(sr - sc) > 0.1 * max(sr, sc):
             assert gpu_rows == (variant == "normuon" or sr >= sc), (sr, sc)
         ref = oracle.normuon_rows(O) if gpu_rows else oracle.normuon_cols(O)
         step = 0.02 * 0.2 * math.sqrt(max(shape))

@@ -174,6 +174,27 @@ int muon_step_grouped(const muon_group* groups, int ngroups, int dtype,
                       void* workspace, size_t workspace_bytes, float* stats, void* stream);
 
 /*
+ * muon_step_grouped without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of MUON_NOALLOC_WORKSPACE_BYTES inside the library (each GPU the library
+ * runs on holds its own copy until the process ends); a call whose groups
+ * need more (muon_workspace_bytes_grouped) returns
+ * MUON_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The call
+ * allocates nothing: on its first call on a device it looks up that device's
+ * copy of the array (hipGetSymbolAddress, with the device current).  Every
+ * call on one GPU shares that GPU's array and its contents are ignored on
+ * entry, so calls that overlap in time on one GPU (different streams, or
+ * different host threads) race and must be serialised by the caller.  Other
+ * arguments, results and errors are those of muon_step_grouped.
+ */
+#define MUON_NOALLOC_WORKSPACE_BYTES (((size_t)64) << 20)
+int muon_step_grouped_noalloc(const muon_group* groups, int ngroups, int dtype,
+                              double lr, double momentum, double weight_decay, int ns_steps,
+                              double a, double b, double c, int variant,
+                              float* stats, void* stream);
+
+/*
  * AdamW for the parameters a hybrid Muon optimizer keeps off Muon: the input
  * embedding, the output head and the gains and biases ("LLM Pretraining Loss
  * Spike 진단과 처방" (juhoplayground.github.io), section "Muon head의 실체는

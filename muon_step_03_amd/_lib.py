@@ -31,13 +31,14 @@ MUON_MAX_NS_STEPS = 100
 MUON_GROUPS_PER_LAUNCH = 8
 MUON_ADAMW_MAX_ELEMENTS = 1 << 40
 MUON_ADAMW_TENSORS_PER_LAUNCH = 32
+MUON_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 # Every symbol include/muon.h declares.
 EXPORTS = (
     "muon_workspace_bytes", "muon_workspace_bytes_grouped", "muon_step",
     "muon_step_batched", "muon_step_grouped", "muon_status_string", "muon_last_hip_error",
     "muon_profile_enable", "muon_profile_read", "muon_phase_name",
-    "muon_adamw_step", "muon_adamw_step_grouped",
+    "muon_adamw_step", "muon_adamw_step_grouped", "muon_step_grouped_noalloc",
 )
 MUON_NUM_PHASES = 10
 
@@ -97,6 +98,9 @@ def lib():
     L.muon_step_batched.restype = ctypes.c_int
     L.muon_step_grouped.argtypes = [ctypes.POINTER(MuonGroup), ctypes.c_int] + _STEP_SCALARS
     L.muon_step_grouped.restype = ctypes.c_int
+    L.muon_step_grouped_noalloc.argtypes = ([ctypes.POINTER(MuonGroup), ctypes.c_int]
+                                            + _STEP_SCALARS[:9] + [ctypes.c_void_p, ctypes.c_void_p])
+    L.muon_step_grouped_noalloc.restype = ctypes.c_int
     L.muon_status_string.argtypes = [ctypes.c_int]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_last_hip_error.argtypes = []

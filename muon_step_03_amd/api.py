@@ -313,6 +313,27 @@ def muon_step_grouped(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, l
         _keep_for_stream(stream, ws)
 
 
+def muon_step_grouped_noalloc(groups: Sequence[_lib.MuonGroup], dtype: torch.dtype, *, lr=0.02,
+                              momentum=0.95, weight_decay=0.1, ns_steps=5,
+                              ns_coefficients=NS_COEFFICIENTS, variant="muon", scale="moonlight",
+                              stats=None, stream=None, device=None):
+    """:func:`muon_step_grouped` on the library's static workspace
+    (``MUON_NOALLOC_WORKSPACE_BYTES`` per GPU): nothing is allocated, here
+    or in the library.  Calls that overlap in time on one GPU share that
+    workspace and must be serialised by the caller."""
+    groups = list(groups)
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    check_stats(stats, sum(int(g.count) for g in groups), device)
+    arr = _groups_array(groups)
+    st = _lib.lib().muon_step_grouped_noalloc(
+        arr, len(groups),
+        *_scalars(dtype_code(dtype), lr, momentum, weight_decay, ns_steps, ns_coefficients,
+                  variant, scale),
+        _ptr(stats), _stream_handle(stream))
+    _check(st, "muon_step_grouped_noalloc")
+
+
 class MuonStep:
     """Muon (or MuonGS) for a list of 2-D hidden weights.
 

@@ -264,9 +264,12 @@ struct Sel {
   int64_t stats_index;  // first matrix of the group in the stats array
 };
 
-int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, double momentum,
-               double wd, int ns_steps, double a, double b, double c, int variant,
-               void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+// Every check that needs no workspace: dtype, scalars, groups and the launch
+// size limits.  Sets the workspace bytes the call needs (0 for an empty
+// batch) and the number of matrices.
+int validate_groups(const muon_group* groups, int ngroups, int dtype, double lr, double momentum,
+                    double wd, int ns_steps, double a, double b, double c, int variant,
+                    size_t* need_out, int64_t* n_out) {
   if (!dtype_ok(dtype)) return MUON_ERR_UNSUPPORTED_DTYPE;
   int st = check_scalars(lr, momentum, wd, ns_steps, a, b, c, variant);
   if (st != MUON_OK) return st;
@@ -292,8 +295,20 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     need += L.total;
     n_matrices += groups[i].count;
   }
+  *need_out = n_matrices ? need + kAlign : 0;
+  *n_out = n_matrices;
+  return MUON_OK;
+}
+
+int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, double momentum,
+               double wd, int ns_steps, double a, double b, double c, int variant,
+               void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  size_t need = 0;
+  int64_t n_matrices = 0;
+  int st = validate_groups(groups, ngroups, dtype, lr, momentum, wd, ns_steps, a, b, c, variant,
+                           &need, &n_matrices);
+  if (st != MUON_OK) return st;
   if (n_matrices == 0) return MUON_OK;  // empty batch: nothing to do
-  need += kAlign;
   if (!workspace) return MUON_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return MUON_ERR_WORKSPACE_TOO_SMALL;
   for (int i = 0; i < ngroups; ++i) {
@@ -627,6 +642,37 @@ int run_adamw(const muon_adamw_tensor* t, int64_t count, int dtype, double beta1
   return flush();
 }
 
+// ---- the workspace of muon_step_grouped_noalloc: one static array per GPU
+// (each device holds its own copy while the process lives).  Host code never
+// uses the array's name as an address: its device address is looked up once
+// per device with hipGetSymbolAddress (with that device current) and kept.
+constexpr size_t kScratchBytes = MUON_NOALLOC_WORKSPACE_BYTES;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of the current device's scratch array (null on a HIP error,
+// which is then kept for muon_last_hip_error).
+void* scratch_on_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    g_last_hip_error = int(e != hipSuccess ? e : hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = int(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -710,6 +756,22 @@ int muon_step_grouped(const muon_group* groups, int ngroups, int dtype, double l
                       void* workspace, size_t workspace_bytes, float* stats, void* stream) {
   return run_groups(groups, ngroups, dtype, lr, momentum, weight_decay, ns_steps, a, b, c,
                     variant, workspace, workspace_bytes, stats, stream);
+}
+
+int muon_step_grouped_noalloc(const muon_group* groups, int ngroups, int dtype, double lr,
+                              double momentum, double weight_decay, int ns_steps, double a,
+                              double b, double c, int variant, float* stats, void* stream) {
+  size_t need = 0;
+  int64_t n_matrices = 0;
+  const int st = validate_groups(groups, ngroups, dtype, lr, momentum, weight_decay, ns_steps, a, b,
+                                 c, variant, &need, &n_matrices);
+  if (st != MUON_OK) return st;
+  if (n_matrices == 0) return MUON_OK;
+  if (need > kScratchBytes) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MUON_ERR_HIP;
+  return run_groups(groups, ngroups, dtype, lr, momentum, weight_decay, ns_steps, a, b, c, variant,
+                    ws, kScratchBytes, stats, stream);
 }
 
 const char* muon_status_string(int status) {

@@ -320,3 +320,21 @@ def test_stats_buffer_checks():
         check_stats(torch.zeros(10), 2)
     with pytest.raises(TypeError):
         check_stats([0.0] * 10, 2)
+
+
+def test_noalloc_validation(L):
+    """muon_step_grouped_noalloc validates like muon_step_grouped and refuses
+    groups whose workspace exceeds its static array, before any HIP call."""
+    def call(groups, dtype=1, ns=5, variant=0):
+        arr = (_lib.MuonGroup * max(1, len(groups)))(*groups)
+        return L.muon_step_grouped_noalloc(arr, len(groups), dtype, 0.02, 0.95, 0.1, ns,
+                                           3.4445, -4.775, 2.0315, variant, None, None)
+    big = _lib.MuonGroup(8, 1024, 4096, None, None, None, W, G, M)
+    assert L.muon_workspace_bytes_grouped((_lib.MuonGroup * 1)(big), 1, 1) > \
+        _lib.MUON_NOALLOC_WORKSPACE_BYTES
+    assert call([big]) == _lib.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert call([big], dtype=7) == _lib.MUON_ERR_UNSUPPORTED_DTYPE
+    assert call([big], ns=-1) == _lib.MUON_ERR_INVALID_ARGUMENT
+    assert call([_lib.MuonGroup(1, 0, 5, None, None, None, W, G, M)]) == _lib.MUON_ERR_INVALID_SHAPE
+    assert call([_lib.MuonGroup(0, 5, 5, None, None, None, None, None, None)]) == _lib.MUON_OK
+    assert call([]) == _lib.MUON_OK

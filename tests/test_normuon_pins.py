@@ -170,3 +170,44 @@ def test_meqmuon_cases_cover_both_directions():
         O = -(Wm - (1 - 0.002) * W) / (0.02 * 0.2 * math.sqrt(max(shape)))
         seen.add(meqmuon_direction(O))
     assert seen == {"rows", "cols"}
+
+
+# Shapes on both sides of square, from nearly square to very elongated.
+FORCED_SHAPES = [(4, 9), (9, 4), (16, 40), (40, 16), (3, 100), (100, 3), (64, 256), (256, 64),
+                 (31, 33), (33, 31)]
+
+
+@pytest.mark.parametrize("shape", FORCED_SHAPES)
+def test_meqmuon_forced_direction(shape):
+    """The cases the page's sentence decides on its own (MeqMuon picks the
+    direction that is imbalanced): in a semi-orthogonal O the short side's
+    vectors all have norm 1 (spread 0) while the long side's differ, so the
+    long side's vectors are equalised — columns of a wide O, rows of a tall
+    one — whatever rule settles two imbalanced directions."""
+    rng = np.random.default_rng(61 + shape[0] + 7 * shape[1])
+    Q = semi_orthogonal(*shape, rng)
+    wide = shape[0] < shape[1]
+    assert meqmuon_direction(Q) == ("cols" if wide else "rows")
+    assert meqmuon_direction(2.5 * Q) == ("cols" if wide else "rows")
+
+
+@pytest.mark.parametrize("shape", FORCED_SHAPES)
+def test_meqmuon_forced_step(shape):
+    """The whole step on a semi-orthogonal gradient Q (M = 0): O = f^5(x0) Q
+    keeps Q's equal short-side norms, so MeqMuon's step is Muon's with the
+    long side's vectors of O equalised (brute force), and NorMuon's equals
+    it for a tall W (rows are the long side's vectors there)."""
+    rng = np.random.default_rng(62 + shape[0] + 7 * shape[1])
+    W = rng.standard_normal(shape) * 0.02
+    Q = semi_orthogonal(*shape, rng)
+    M0 = np.zeros(shape)
+    Wq, _, _ = muon_step(W, Q, M0, variant="meqmuon")
+    Wm, _, _ = muon_step(W, Q, M0, variant="muon")
+    d, step = 1 - 0.02 * 0.1, 0.02 * 0.2 * math.sqrt(max(shape))
+    O = -(Wm - d * W) / step
+    wide = shape[0] < shape[1]
+    expect = d * W - step * (brute_rows(O.T).T if wide else brute_rows(O))
+    assert np.max(np.abs(Wq - expect)) < 1e-14
+    if not wide:
+        Wr, _, _ = muon_step(W, Q, M0, variant="normuon")
+        assert np.max(np.abs(Wq - Wr)) < 1e-15

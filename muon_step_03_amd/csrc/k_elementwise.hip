@@ -113,10 +113,11 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
   // A wide matrix (X = U, no transpose) is taken in tiles of 16 rows x 256
-  // columns (row runs of 512 / 1024 bytes of G / M), a tall one in 64 x 64
-  // tiles transposed through LDS; both shapes give the same tile count.
-  const bool flat = !g.trans && (g.q_pad % (4 * T)) == 0;
-  const int TR = flat ? T / 4 : T, TC = flat ? 4 * T : T;
+  // columns (row runs of 512 / 1024 bytes of G / M), or of 32 x 128 when its
+  // padded row length is a multiple of 128 only; a tall one in 64 x 64
+  // tiles transposed through LDS.  All give the same tile count.
+  const int flat = g.trans ? 1 : (g.q_pad % (4 * T)) == 0 ? 4 : (g.q_pad % (2 * T)) == 0 ? 2 : 1;
+  const int TR = T / flat, TC = T * flat;
   const int ntj = g.q_pad / TC;
   const int ti = tr.tile / ntj;
   const int tj = tr.tile - ti * ntj;

@@ -136,6 +136,19 @@ struct CfgUpdBig {
   static constexpr int STAGES = 4;
   static constexpr int OCC = 1;
 };
+// Update of matrices whose padded short side is 512 (MoE experts): 512x128
+// tiles, 8 waves of 128x64 (the wave tile of the 256x256 update), one block
+// per CU, three stages of 40 KiB.  A tile spans the whole short side, so the
+// long side is padded to a multiple of 128 only: 1408 stays 1408 (the
+// 256-wide tiles pad it to 1536, 9 % more work and X traffic), and a
+// matrix's 512x512 B, read by each of its long-side tiles, stays in L2.
+struct CfgUpd512 {
+  static constexpr int BM = 512, BN = 128, NW = 8, WGM = 4, WGN = 2;
+  static constexpr int WM = BM / (32 * WGM), WN = BN / (32 * WGN);
+  static constexpr int BK = 32;
+  static constexpr int STAGES = 3;
+  static constexpr int OCC = 1;
+};
 template <>
 struct Cfg<MODE_UPDATE> {
   static constexpr int BM = kUpdTileM, BN = kUpdTileN, NW = kUpdWaves, WGM = MUON_UPD_WGM,
@@ -448,8 +461,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // own loads of it at the end of its phase before that barrier.
   const bool late = wave >= 4;
   issue(std::integral_constant<int, 0>{}, dg, 0);
-  if (1 < nk) issue(std::integral_constant<int, 1>{}, dg, 1);
-  if constexpr (S > 2) if (2 < nk) issue(std::integral_constant<int, (S > 2 ? 2 : 0)>{}, dg, 2);
+  if constexpr (S > 2) if (1 < nk) issue(std::integral_constant<int, 1>{}, dg, 1);
+  if constexpr (S > 3) if (2 < nk) issue(std::integral_constant<int, (S > 3 ? 2 : 0)>{}, dg, 2);
   wait_stage(dg, 0, S - 2);  // the prologue issued steps 0 .. S-2
   block_barrier();
   if (late) block_barrier();
@@ -538,12 +551,15 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= (MODE == MODE_POLY ? cc : alpha);
   // fp32 staging row pitch (floats): 4 mod 64 banks, so the 16-byte writes of
-  // 16 lanes (16 consecutive rows, one column) cover all banks once.
+  // 16 lanes (16 consecutive rows, one column) cover all banks once.  Passes
+  // of PR rows: 64, or 128 for the 512-row tiles (the same bytes per pass).
   constexpr int TP = BN + 4;
-  static_assert(64 * TP * 4 <= S * STAGE_BYTES, "staging");
+  constexpr int PR = BM == 512 ? 128 : 64;
+  static_assert(PR * TP * 4 <= S * STAGE_BYTES, "staging");
   LDS_AS float* T = (LDS_AS float*)smem;
+  auto tix = [](int r, int c) { return r * TP + c; };   // staging element (r, c)
   constexpr int CPR = BN / 8;                // 8-element chunks per row
-  constexpr int CHUNKS = 64 * CPR / NT;      // per thread per pass
+  constexpr int CHUNKS = PR * CPR / NT;      // per thread per pass
   uint16_t* Cout = MODE == MODE_UPDATE ? Xout : (MODE == MODE_GRAM ? Am : Bm);
   const int64_t ldc = MODE == MODE_UPDATE ? qp : pp;
   // Output element (r, c): row-major, except the polynomial's B, which the
@@ -556,20 +572,20 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   };
 
 
-  // Pass `pass` stages tile rows 64 pass .. +63: the 32-row accumulator
-  // blocks wm*WM + mi with (wm*WM + mi) / 2 == pass.
+  // Pass `pass` stages tile rows PR pass .. +PR-1: the 32-row accumulator
+  // blocks wm*WM + mi with (wm*WM + mi) / (PR/32) == pass.
   auto stage = [&](int pass) {
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi) {
       const int blk = wm * WM + mi;
-      if ((blk >> 1) != pass) continue;
-      const int row = (blk & 1) * 32 + (lane & 31);
+      if (blk / (PR / 32) != pass) continue;
+      const int row = (blk % (PR / 32)) * 32 + (lane & 31);
 #pragma unroll
       for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int col = wn * 32 * WN + ni * 32 + 8 * g4 + 4 * (lane >> 5);
-          *(LDS_AS f32x4_t*)(T + row * TP + col) =
+          *(LDS_AS f32x4_t*)(T + tix(row, col)) =
               f32x4_t{acc[mi][ni][4 * g4], acc[mi][ni][4 * g4 + 1], acc[mi][ni][4 * g4 + 2],
                       acc[mi][ni][4 * g4 + 3]};
         }
@@ -587,6 +603,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   constexpr bool kStageT = C::NW == 4;
   constexpr int TPT = 68;
   static_assert(MODE == MODE_UPDATE || BN * TPT * 4 <= S * STAGE_BYTES, "transposed staging");
+  static_assert(MODE == MODE_UPDATE || PR == 64, "symmetric tiles stage 64-row passes");
   // Mirrored chunk q: tile column c (a row of the mirrored block), rows
   // r8 .. r8+7 of the pass.
   auto mirror_pos = [&](int q, int& c, int& r8) {
@@ -623,7 +640,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // 16-byte rows of A (L2-resident: its K steps just streamed through).  A
   // is symmetric, so a mirrored chunk's term is again a row segment of A.
   constexpr bool kLin = MODE == MODE_POLY;
-  constexpr int MCH = BN * 8 / NT;           // mirrored chunks per thread per pass
+  constexpr int MCH = BN * (PR / 8) / NT;    // mirrored chunks per thread per pass
   const uint16_t* Lin = Am;
   const float lin_coef = cb;
   auto add_lin = [&](float (&v)[8], const uint4& x) {
@@ -642,14 +659,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       for (int u = 0; u < CHUNKS; ++u) {
         const int q = t + NT * u;
         const int row = q / CPR, col = (q % CPR) * 8;
-        lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + 64 * pass + row) * ldc + j0 + col);
+        lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + PR * pass + row) * ldc + j0 + col);
       }
       if (mirror) {
 #pragma unroll
         for (int u = 0; u < MCH; ++u) {
           int c, r8;
           mirror_pos(t + NT * u, c, r8);
-          lin_m[u] = *reinterpret_cast<const uint4*>(Lin + (j0 + c) * ldc + i0 + 64 * pass + r8);
+          lin_m[u] = *reinterpret_cast<const uint4*>(Lin + (j0 + c) * ldc + i0 + PR * pass + r8);
         }
       }
     }
@@ -661,15 +678,15 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       const int q = t + NT * u;
       const int row = q / CPR, col = (q % CPR) * 8;
       float v[8];
-      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
-      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
+      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + tix(row, col));
+      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + tix(row, col + 4));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[e] = v0[e];
         v[e + 4] = v1[e];
       }
       if (kLin) add_lin(v, lin[u]);
-      *reinterpret_cast<uint4*>(out_at(i0 + 64 * pass + row, j0 + col)) = pack8(v);
+      *reinterpret_cast<uint4*>(out_at(i0 + PR * pass + row, j0 + col)) = pack8(v);
     }
   };
   // Mirrored block: rows j0 + c of C (c < BN), columns i0 + 64*pass + r8 ..
@@ -691,10 +708,10 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
+        for (int e = 0; e < 8; ++e) v[e] = T[tix(r8 + e, c)];
       }
       if (kLin) add_lin(v, lin_m[u]);
-      *reinterpret_cast<uint4*>(out_at(j0 + c, i0 + 64 * pass + r8)) = pack8(v);
+      *reinterpret_cast<uint4*>(out_at(j0 + c, i0 + PR * pass + r8)) = pack8(v);
     }
   };
 
@@ -754,7 +771,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       for (int u = 0; u < GS; ++u) {
         const int q = t + NT * (u0 + u);
         const int row = q / CPR, col = (q % CPR) * 8;
-        const int i = i0 + 64 * pass + row, j = j0 + col;
+        const int i = i0 + PR * pass + row, j = j0 + col;
         wv[u] = make_uint4(0, 0, 0, 0);
         if (!g.trans && wvec && i < g.p && j < g.q)
           wv[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(i) * wld + j);
@@ -764,14 +781,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         const int q = t + NT * (u0 + u);
         const int row = q / CPR, col = (q % CPR) * 8;
         float v[8];
-        const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + row * TP + col);
-        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + row * TP + col + 4);
+        const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + tix(row, col));
+        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + tix(row, col + 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           v[e] = v0[e];
           v[e + 4] = v1[e];
         }
-        const int i = i0 + 64 * pass + row, j = j0 + col;
+        const int i = i0 + PR * pass + row, j = j0 + col;
         if (!g.trans) {
           if (i < g.p && j < g.q) {
             uint16_t* wp = Wm + int64_t(i) * wld + j;
@@ -782,18 +799,19 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
           }
         } else {
           // O is needed by columns: keep the complete values in T
-          *(LDS_AS f32x4_t*)(T + row * TP + col) = f32x4_t{v[0], v[1], v[2], v[3]};
-          *(LDS_AS f32x4_t*)(T + row * TP + col + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+          *(LDS_AS f32x4_t*)(T + tix(row, col)) = f32x4_t{v[0], v[1], v[2], v[3]};
+          *(LDS_AS f32x4_t*)(T + tix(row, col + 4)) = f32x4_t{v[4], v[5], v[6], v[7]};
         }
       }
     }
     if (g.trans) {
-      constexpr int MC = BN * 8 / NT;
+      constexpr int MC = BN * (PR / 8) / NT;
       constexpr int MGS = (C::NW == 8 || MC < MUON_TAIL_GS) ? MC : MUON_TAIL_GS;
       static_assert(MC % MGS == 0, "mirrored chunk groups");
-      // W row j0 + c, columns i0 + 64 pass + r8 .. +7, from staged column c;
-      // 8 consecutive lanes take the 8 chunks of one row, so that every W
-      // load and W' store instruction covers 8 whole 128-byte row runs (the
+      // W row j0 + c, columns i0 + PR pass + r8 .. +7, from staged column c;
+      // 8 consecutive lanes take 8 chunks of one row (the pass's first 64
+      // columns, then the next 64 when PR = 128), so that every W load and
+      // W' store instruction covers 8 whole 128-byte row runs (the
       // column reads of T then meet 4-way bank conflicts; measured faster
       // than one row per lane: GPT-160M last update 221 -> 214 us).  The
       // first group's W loads are issued before the barrier.
@@ -802,8 +820,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < MGS; ++u) {
           const int q = t + NT * (u0 + u);
-          const int c = (q >> 3) % BN, r8 = (q & 7) * 8;
-          const int i = i0 + 64 * pass + r8, j = j0 + c;
+          const int c = (q >> 3) % BN, r8 = ((q & 7) + 8 * (q / (8 * BN))) * 8;
+          const int i = i0 + PR * pass + r8, j = j0 + c;
           wt[u] = make_uint4(0, 0, 0, 0);
           if (wvec && j < g.q && i < g.p) wt[u] = *reinterpret_cast<const uint4*>(Wm + int64_t(j) * wld + i);
         }
@@ -816,12 +834,12 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < MGS; ++u) {
           const int q = t + NT * (u0 + u);
-          const int c = (q >> 3) % BN, r8 = (q & 7) * 8;
-          const int i = i0 + 64 * pass + r8, j = j0 + c;
+          const int c = (q >> 3) % BN, r8 = ((q & 7) + 8 * (q / (8 * BN))) * 8;
+          const int i = i0 + PR * pass + r8, j = j0 + c;
           if (j >= g.q || i >= g.p) continue;
           float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = T[(r8 + e) * TP + c];
+          for (int e = 0; e < 8; ++e) v[e] = T[tix(r8 + e, c)];
           uint16_t* wp = Wm + int64_t(j) * wld + i;
           if (wvec)
             *reinterpret_cast<uint4*>(wp) = w_apply(wt[u], v);
@@ -833,7 +851,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   };
 
 #pragma unroll
-  for (int pass = 0; pass < BM / 64; ++pass) {
+  for (int pass = 0; pass < BM / PR; ++pass) {
     // The polynomial's b*A loads are issued before the pass's staging and
     // barriers where registers allow (64x64 wave tiles, and the 256x256
     // tiles, whose one block per CU has no other block to hide their latency
@@ -846,9 +864,9 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     block_barrier();
     if (MODE == MODE_POLY && ti == tj) {
       // a*I on a diagonal tile (i0 == j0): staged row r of this pass holds
-      // its diagonal element in column 64 pass + r; the padding rows beyond
+      // its diagonal element in column PR pass + r; the padding rows beyond
       // p keep a zero diagonal
-      if (t < 64 && i0 + 64 * pass + t < g.p) T[t * TP + 64 * pass + t] += ca;
+      if (t < PR && i0 + PR * pass + t < g.p) T[tix(t, PR * pass + t)] += ca;
       block_barrier();
     }
     if (fuse) {
@@ -896,8 +914,11 @@ hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float a, float 
                        dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, a, b, c);
   return hipGetLastError();
 }
-hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s) {
-  if (big)
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, int cfg, hipStream_t s) {
+  if (cfg == kUpdCfg512)
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, CfgUpd512>), grid_of(tl), dim3(64 * CfgUpd512::NW),
+                       0, s, bt, tl, iter, 0.f, 0.f, 0.f);
+  else if (cfg == kUpdCfg256)
     hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, CfgUpdBig>), grid_of(tl), dim3(64 * CfgUpdBig::NW),
                        0, s, bt, tl, iter, 0.f, 0.f, 0.f);
   else

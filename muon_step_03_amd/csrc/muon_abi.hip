@@ -66,8 +66,10 @@ Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
   L.trans = rows > cols ? 1 : 0;
   L.p = rows < cols ? rows : cols;
   L.q = rows < cols ? cols : rows;
-  L.tile_n = dtype == MUON_DTYPE_BF16 ? kBf16PadQ : kF32Tile;
   L.p_pad = round_up(L.p, L.tile);
+  // bf16: the long side is padded to the update's column tile, 256, or 128
+  // for a padded short side of 512 (the 512x128 update tiles)
+  L.tile_n = dtype != MUON_DTYPE_BF16 ? kF32Tile : (L.p_pad == kUpd512P ? kUpd512TileN : kBf16PadQ);
   L.q_pad = round_up(L.q, L.tile_n);
   L.head_tiles = (L.p_pad / kEwTile) * (L.q_pad / kEwTile);
   L.tail_tiles_c = cdiv(cols, kEwTile);
@@ -140,10 +142,17 @@ int check_group(const muon_group& g, int dtype) {
 struct PhaseTiles {
   int64_t head, gram, update, tail;
 };
-// bf16 matrices that may take 256x256 tiles (whether they do depends on the
-// launch: see the tile lists in run_groups).
-bool big_eligible(const Layout& L, bool bf16) {
-  return bf16 && L.p >= kBigMinP && L.p_pad % kBigTile == 0 && L.q_pad % kBigTile == 0;
+// bf16 matrices whose symmetric products may take 256x256 tiles (whether
+// they do depends on the launch: see the tile lists in run_groups).
+bool syrk_big_eligible(const Layout& L, bool bf16) {
+  return bf16 && L.p >= kBigMinP && L.p_pad % kBigTile == 0;
+}
+// bf16 matrices whose update takes the 512x128 tiles (always: their long
+// side is padded to a multiple of 128 only).
+bool upd512(const Layout& L, bool bf16) { return bf16 && L.p_pad == kUpd512P; }
+// bf16 matrices whose update may take 256x256 tiles.
+bool upd_big_eligible(const Layout& L, bool bf16) {
+  return syrk_big_eligible(L, bf16) && !upd512(L, bf16) && L.q_pad % kBigTile == 0;
 }
 PhaseTiles phase_tiles(const Layout& L, bool bf16) {
   PhaseTiles t;
@@ -151,7 +160,9 @@ PhaseTiles phase_tiles(const Layout& L, bool bf16) {
   const int64_t nt = L.p_pad / ts;
   t.head = L.head_tiles;
   t.gram = nt * (nt + 1) / 2;
-  t.update = bf16 ? (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN) : nt * (L.q_pad / kF32Tile);
+  t.update = !bf16 ? nt * (L.q_pad / kF32Tile)
+                   : upd512(L, bf16) ? L.q_pad / kUpd512TileN
+                                     : (L.p_pad / kUpdTileM) * (L.q_pad / kUpdTileN);
   t.tail = L.tail_tiles;
   return t;
 }
@@ -426,7 +437,8 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     for (int k = 0; k < nsel; ++k) any_fused = any_fused || bt.g[k].fuse;
     // Symmetric products: one launch over the groups in 128x128 tiles and
     // one over the large groups in 256x256 tiles (each only if non-empty).
-    TileList tl_gram{}, tl_poly{}, tl_gram_big{}, tl_poly_big{}, tl_upd{}, tl_upd_big{};
+    TileList tl_gram{}, tl_poly{}, tl_gram_big{}, tl_poly_big{}, tl_upd{}, tl_upd_big{},
+        tl_upd_512{};
     if (bf16) {
       const int cpx = cus_per_xcd();
       if (cpx == 0) {
@@ -439,19 +451,21 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       // update tiles).
       int64_t big_syrk = 0, big_upd = 0;
       for (int k = 0; k < nsel; ++k) {
-        if (!big_eligible(sel[k].L, true)) continue;
+        if (!syrk_big_eligible(sel[k].L, true)) continue;
         const int64_t nb = sel[k].L.p_pad / kBigTile;
         big_syrk += bt.g[k].count * (nb * (nb + 1) / 2);
-        big_upd += bt.g[k].count * nb * (sel[k].L.q_pad / kBigTile);
+        if (upd_big_eligible(sel[k].L, true))
+          big_upd += bt.g[k].count * nb * (sel[k].L.q_pad / kBigTile);
       }
       const bool use_big_syrk = big_syrk >= int64_t(kSyrkBigMinRounds) * 8 * cpx;
       const bool use_big_upd = big_upd >= int64_t(kUpdBigMinRounds) * 8 * cpx;
       int64_t nt[kMaxGroups], ntb[kMaxGroups], npt[kMaxGroups], nptb[kMaxGroups], nu[kMaxGroups],
-          nub[kMaxGroups], kq[kMaxGroups], kp[kMaxGroups];
+          nub[kMaxGroups], nu5[kMaxGroups], kq[kMaxGroups], kp[kMaxGroups];
       for (int k = 0; k < nsel; ++k) {
         const Layout& L = sel[k].L;
-        const bool elig = big_eligible(L, true);
-        const bool big = use_big_syrk && elig, ubig = use_big_upd && elig;
+        const bool big = use_big_syrk && syrk_big_eligible(L, true);
+        const bool ubig = use_big_upd && upd_big_eligible(L, true);
+        const bool u512 = upd512(L, true);
         const int64_t nb = L.p_pad / kBigTile;
         nt[k] = big ? 0 : w_gram.tiles[k];
         ntb[k] = big ? nb * (nb + 1) / 2 : 0;
@@ -463,8 +477,9 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
         const bool pbig = big && L.p >= kPolyBigMinP;
         npt[k] = pbig ? 0 : w_gram.tiles[k];
         nptb[k] = pbig ? nb * (nb + 1) / 2 : 0;
-        nu[k] = ubig ? 0 : w_upd.tiles[k];
+        nu[k] = (ubig || u512) ? 0 : w_upd.tiles[k];
         nub[k] = ubig ? nb * (L.q_pad / kBigTile) : 0;
+        nu5[k] = u512 ? w_upd.tiles[k] : 0;
         kq[k] = bt.g[k].q_pad;
         kp[k] = bt.g[k].p_pad;
       }
@@ -474,6 +489,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       tl_poly_big = make_tile_list(bt, nptb, kp, kBigBlocksPerCU * cpx);
       tl_upd = make_tile_list(bt, nu, kp, kUpdBlocksPerCU * cpx);
       tl_upd_big = make_tile_list(bt, nub, kp, kBigBlocksPerCU * cpx);
+      tl_upd_512 = make_tile_list(bt, nu5, kp, kBigBlocksPerCU * cpx);
     }
     hipEvent_t t0 = nullptr;
     Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};
@@ -501,11 +517,11 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
           return st;
         const int fuse_tail = (it == ns_steps - 1 && any_fused) ? 1 : 0;
         const int ph = fuse_tail ? kPhaseUpdateTail : 4;
-        for (int big = 0; big < 2; ++big) {
-          TileList tl = big ? tl_upd_big : tl_upd;
+        for (int cfg = kUpdCfg128; cfg <= kUpdCfg512; ++cfg) {
+          TileList tl = cfg == kUpdCfg512 ? tl_upd_512 : cfg == kUpdCfg256 ? tl_upd_big : tl_upd;
           if (!tl.ngroups) continue;
           tl.fuse_tail = fuse_tail;
-          if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, big != 0, s), ph, s, t0)))
+          if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, cfg, s), ph, s, t0)))
             return st;
         }
       } else {

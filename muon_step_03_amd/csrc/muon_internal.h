@@ -284,7 +284,13 @@ hipError_t launch_gram_bf16(const Batch& bt, const TileList& tl, int iter, bool 
 // is the plain product X' = B X.
 hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float a, float b, float c, bool big,
                             hipStream_t s);
-hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, bool big, hipStream_t s);
+// Update tile configurations: 128x256 (two blocks per CU), 256x256 (one
+// block per CU) and 512x128 (one block per CU, matrices whose padded short
+// side is 512: their long side is padded to a multiple of 128 only).
+enum : int { kUpdCfg128 = 0, kUpdCfg256 = 1, kUpdCfg512 = 2 };
+constexpr int kUpd512P = 512;
+constexpr int kUpd512TileN = 128;
+hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, int cfg, hipStream_t s);
 hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s);
 hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s);
 hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s);

@@ -55,7 +55,10 @@ def ws_formula(count, rows, cols, dtype):
     tile_p, tile_q = (128, 256) if dtype == _lib.MUON_DTYPE_BF16 else (64, 64)
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     p, q = min(rows, cols), max(rows, cols)
-    pp, qp = -(-p // tile_p) * tile_p, -(-q // tile_q) * tile_q
+    pp = -(-p // tile_p) * tile_p
+    if dtype == _lib.MUON_DTYPE_BF16 and pp == 512:
+        tile_q = 128          # the 512x128 update tiles: long side padded to 128
+    qp = -(-q // tile_q) * tile_q
     es = ES[dtype]
     head = (pp // 64) * (qp // 64)
     tail = math.ceil(rows / 64) * math.ceil(cols / 64)
@@ -66,7 +69,7 @@ def ws_formula(count, rows, cols, dtype):
 
 
 @pytest.mark.parametrize("shape", [(256, 512), (768, 3072), (3072, 768), (100, 300), (1, 1),
-                                   (1408, 512), (2048, 5632)])
+                                   (1408, 512), (512, 1408), (450, 777), (2048, 5632)])
 @pytest.mark.parametrize("dtype", [_lib.MUON_DTYPE_F32, _lib.MUON_DTYPE_BF16])
 @pytest.mark.parametrize("count", [1, 7])
 def test_workspace_bytes(L, shape, dtype, count):

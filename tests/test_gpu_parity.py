@@ -126,6 +126,43 @@ def test_bf16_large_tiles(variant, stats):
         print(f"bf16 {shapes[gi][1:]} #{i} {variant} stats={stats}: relF(dW) = {e:.2e}")
 
 
+# Short sides padded to 512 take the 512x128 update tiles (one tile spans the
+# short side; the long side is padded to a multiple of 128): ragged short and
+# long sides, wide and tall, with the step applied by the last update (no
+# statistics) and by the separate tail (MuonGS with statistics), in a grouped
+# call like the MoE experts'.
+SHORT512 = [(3, 400, 1000), (2, 1000, 400), (2, 450, 777), (2, 777, 450), (2, 512, 512),
+            (3, 500, 1408), (2, 1408, 512)]
+
+
+@pytest.mark.parametrize("variant,with_stats", [("muon", False), ("muongs", True)])
+def test_bf16_short_side_512(variant, with_stats):
+    Ws = [wl.random_matrix(c * r, k, 0.02, 1100 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(SHORT512)]
+    Gs = [wl.random_matrix(c * r, k, 1e-3, 1150 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(SHORT512)]
+    Ms = [wl.random_matrix(c * r, k, 1e-3, 1200 + i, torch.float32, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(SHORT512)]
+    W0 = [w.clone() for w in Ws]
+    M0 = [m.clone() for m in Ms]
+    n = sum(c for c, _, _ in SHORT512)
+    st = torch.full((5 * n,), float("nan"), device=DEV) if with_stats else None
+    muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Ws, Gs, Ms)], torch.bfloat16,
+                      variant=variant, stats=st, **HP)
+    torch.cuda.synchronize()
+    k = 0
+    for gi, (c, r, cols) in enumerate(SHORT512):
+        for i in range(c):
+            s5 = st[5 * k:5 * k + 5] if with_stats else None
+            e, _, _ = check_against_oracle(W0[gi][i], Gs[gi][i], M0[gi][i], Ws[gi][i], Ms[gi][i],
+                                           variant=variant, stats=s5)
+            if variant == "muongs":
+                check_muongs_invariants(W0[gi][i], Ws[gi][i], 0.02, 0.1, cos_tol=1e-3,
+                                        r2_tol=1e-3, ratio_max=1.01)
+            k += 1
+        print(f"{r}x{cols} {variant}: relF(dW) = {e:.2e}")
+
+
 # Plain Muon without statistics: on the bf16 path the last Newton-Schulz
 # update applies the step to W itself whenever the weight's row length is a
 # multiple of 8 (the other shapes here take the separate tail).
@@ -377,17 +414,23 @@ def slice_boundary_matrices(w):
     n = count x tiles-per-matrix tiles; the tiles per matrix are those of the
     128-wide symmetric tiles ((p_pad/128)(p_pad/128 + 1)/2) and update tiles
     ((p_pad/128)(q_pad/256)), and, for matrices that may take them, of the
-    256x256 ones.  For every boundary b the matrices holding tiles b - 1 and
-    b are returned (one matrix when b falls inside it)."""
+    256x256 ones, or of the 512x128 update tiles (q_pad/128 of them) when the
+    padded short side is 512.  For every boundary b the matrices holding
+    tiles b - 1 and b are returned (one matrix when b falls inside it)."""
     out = set()
     for gi, g in enumerate(w.groups):
         p, q = min(g.rows, g.cols), max(g.rows, g.cols)
-        pp, qp = -(-p // 128) * 128, -(-q // 256) * 256
+        pp = -(-p // 128) * 128
         nt = pp // 128
-        per = {nt * (nt + 1) // 2, nt * (qp // 256)}
-        if p >= 512 and pp % 256 == 0 and qp % 256 == 0:
-            nb = pp // 256
-            per |= {nb * (nb + 1) // 2, nb * (qp // 256)}
+        if pp == 512:
+            qp = -(-q // 128) * 128
+            per = {nt * (nt + 1) // 2, 3, qp // 128}
+        else:
+            qp = -(-q // 256) * 256
+            per = {nt * (nt + 1) // 2, nt * (qp // 256)}
+            if p >= 512 and pp % 256 == 0:
+                nb = pp // 256
+                per |= {nb * (nb + 1) // 2, nb * (qp // 256)}
         for tiles in per:
             n = g.count * tiles
             for x in range(1, 8):

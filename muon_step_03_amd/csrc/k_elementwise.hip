@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
     }
   block_sum3_256(dot, ww, oo, red);
   if (threadIdx.x == 0) {
-    float* p = g.tail_part + (tr.m * g.tail_tiles + tr.tile) * 3;
+    float* p = g.tail_part + (tr.m * g.red_tiles + tr.tile) * 3;
     p[0] = dot;
     p[1] = ww;
     p[2] = oo;
@@ -506,9 +506,9 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
   __shared__ float red[12];
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
-  const float* part = g.tail_part + tr.m * g.tail_tiles * 3;
+  const float* part = g.tail_part + tr.m * g.red_tiles * 3;
   float dot = 0.f, ww = 0.f, oo = 0.f;
-  for (int i = threadIdx.x; i < g.tail_tiles; i += 256) {
+  for (int i = threadIdx.x; i < g.red_tiles; i += 256) {
     dot += part[3 * i + 0];
     ww += part[3 * i + 1];
     oo += part[3 * i + 2];

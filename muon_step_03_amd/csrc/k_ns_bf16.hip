@@ -235,7 +235,12 @@ __device__ __forceinline__ bf16x8_t lds_frag_xT(const LDS_AS char* tile, int kb,
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int MODE, class C>
+// LAST: the update launch of the last iteration, whose groups apply the step
+// (LAST == kLastApply, groups with g.fuse) or write the tail's partial sums
+// (LAST == kLastReduce, groups with g.red) in the epilogue; separate
+// instantiations, so that the other launches carry none of that code (one
+// call never needs both: the step is applied only when nothing is reduced).
+template <int MODE, class C, int LAST = 0>
 __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     Batch bt, TileList tl, int iter, float ca, float cb, float cc) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, S = C::STAGES, BK = C::BK;
@@ -721,7 +726,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   // W (trans).  The host enables it only for bf16 weights whose column count
   // is a multiple of 8, so every 8-element chunk along W's rows is entirely
   // inside or outside the matrix.
-  const bool fuse = MODE == MODE_UPDATE && tl.fuse_tail && g.fuse;
+  const bool fuse = MODE == MODE_UPDATE && LAST == kLastApply && g.fuse;
+  // Fused reduction (last iteration of MuonGS, MuonH, or any step with
+  // statistics): O is stored as usual, and the tile's partial sums of
+  // <W,O>, ||W||^2 and ||O||^2 over the stored bf16 O (what the apply pass
+  // reads) are written to the tail partials, so that no separate pass reads
+  // W and O again before the per-matrix totals.
+  const bool fred = MODE == MODE_UPDATE && LAST == kLastReduce && g.red;
+  float red_dot = 0.f, red_ww = 0.f, red_oo = 0.f;
   // W' = decay W + (-step) O for one 8-element chunk of W at wp (16-byte
   // access when W is 16-byte aligned, element by element otherwise).
   auto w_update = [&](uint16_t* wp, bool wvec, const float (&o)[8]) {
@@ -752,6 +764,99 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       v[2 * e + 1] = fmaf(dec, __uint_as_float(ww[e] & 0xffff0000u), -stp * o[2 * e + 1]);
     }
     return pack8(v);
+  };
+  // Adds one 8-element chunk's terms: o holds the fp32 values, which are
+  // rounded to bf16 first (the stored O), w the W chunk.
+  auto red_add = [&](const float (&o)[8], const uint4& w) {
+    const uint32_t ww4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o0 = bf2f(f2bf(o[2 * e])), o1 = bf2f(f2bf(o[2 * e + 1]));
+      const float w0 = __uint_as_float(ww4[e] << 16), w1 = __uint_as_float(ww4[e] & 0xffff0000u);
+      red_dot = fmaf(w0, o0, fmaf(w1, o1, red_dot));
+      red_ww = fmaf(w0, w0, fmaf(w1, w1, red_ww));
+      red_oo = fmaf(o0, o0, fmaf(o1, o1, red_oo));
+    }
+  };
+  // W chunk of 8 elements at wp: one 16-byte load when W is 16-byte aligned.
+  auto w_chunk = [&](const uint16_t* wp, bool wvec) {
+    if (wvec) return *reinterpret_cast<const uint4*>(wp);
+    uint32_t ww4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ww4[e] = uint32_t(wp[2 * e]) | (uint32_t(wp[2 * e + 1]) << 16);
+    return make_uint4(ww4[0], ww4[1], ww4[2], ww4[3]);
+  };
+  // The fused reduction's pass: O stored by rows (as finish does), the terms
+  // taken by rows for a wide W (W[i][j] = O[i][j]) and by staged columns for
+  // a tall one (W[j][i] = O[i][j]: 8 lanes per W row, as in finish_tail).
+  // The host enables it for row lengths that are multiples of 8 only, so
+  // every chunk along a W row is entirely inside or outside the matrix.
+  auto finish_red = [&](int pass) {
+    const uint16_t* Wm = mat_cptr<uint16_t>(reinterpret_cast<const void* const*>(g.W_tab), g.W, m,
+                                            int64_t(g.rows) * g.cols);
+    const int64_t wld = g.cols;
+    const bool wvec = (reinterpret_cast<uintptr_t>(Wm) & 15) == 0;
+    // all of the pass's W loads are issued together (groups of them made the
+    // register allocation of the 4-wave update spill: 56 to 244 bytes per
+    // lane, none this way)
+    constexpr int RG = CHUNKS;
+    static_assert(CHUNKS % RG == 0, "chunk groups");
+#pragma unroll
+    for (int u0 = 0; u0 < CHUNKS; u0 += RG) {
+      uint4 wv[RG];
+      if (!g.trans) {
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+          const int q = t + NT * (u0 + u);
+          const int row = q / CPR, col = (q % CPR) * 8;
+          const int i = i0 + PR * pass + row, j = j0 + col;
+          wv[u] = make_uint4(0, 0, 0, 0);
+          if (i < g.p && j < g.q) wv[u] = w_chunk(Wm + int64_t(i) * wld + j, wvec);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RG; ++u) {
+        const int q = t + NT * (u0 + u);
+        const int row = q / CPR, col = (q % CPR) * 8;
+        float v[8];
+        const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + tix(row, col));
+        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + tix(row, col + 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = v0[e];
+          v[e + 4] = v1[e];
+        }
+        *reinterpret_cast<uint4*>(out_at(i0 + PR * pass + row, j0 + col)) = pack8(v);
+        // padding rows and columns of O are zero: nothing to add there
+        if (!g.trans) red_add(v, wv[u]);
+      }
+    }
+    if (g.trans) {
+      constexpr int MC = BN * (PR / 8) / NT;
+      constexpr int MRG = MC;
+      static_assert(MC % MRG == 0, "mirrored chunk groups");
+#pragma unroll
+      for (int u0 = 0; u0 < MC; u0 += MRG) {
+        uint4 wt[MRG];
+#pragma unroll
+        for (int u = 0; u < MRG; ++u) {
+          const int q = t + NT * (u0 + u);
+          const int c = (q >> 3) % BN, r8 = ((q & 7) + 8 * (q / (8 * BN))) * 8;
+          const int i = i0 + PR * pass + r8, j = j0 + c;
+          wt[u] = make_uint4(0, 0, 0, 0);
+          if (j < g.q && i < g.p) wt[u] = w_chunk(Wm + int64_t(j) * wld + i, wvec);
+        }
+#pragma unroll
+        for (int u = 0; u < MRG; ++u) {
+          const int q = t + NT * (u0 + u);
+          const int c = (q >> 3) % BN, r8 = ((q & 7) + 8 * (q / (8 * BN))) * 8;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = T[tix(r8 + e, c)];
+          red_add(v, wt[u]);
+        }
+      }
+    }
   };
   auto finish_tail = [&](int pass) {
     uint16_t* Wm = mat_ptr<uint16_t>(g.W_tab, g.W, m, int64_t(g.rows) * g.cols);
@@ -871,6 +976,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     }
     if (fuse) {
       finish_tail(pass);
+    } else if (fred) {
+      finish_red(pass);
     } else {
       if (!kEarlyLin) load_lin(pass, lin, lin_m);
       finish(pass, lin, lin_m);
@@ -885,6 +992,30 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         }
       }
     }
+  }
+  if (fred) {
+    // the tile's three sums, in a fixed order: wave shuffles, then the
+    // waves' values through LDS
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      red_dot += __shfl_xor(red_dot, off, 64);
+      red_ww += __shfl_xor(red_ww, off, 64);
+      red_oo += __shfl_xor(red_oo, off, 64);
+    }
+    __shared__ float red_lds[3 * C::NW];
+    if (lane == 0) {
+      red_lds[wave] = red_dot;
+      red_lds[C::NW + wave] = red_ww;
+      red_lds[2 * C::NW + wave] = red_oo;
+    }
+    block_barrier();
+    if (t < 3) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) sum += red_lds[t * C::NW + w];
+      g.tail_part[(m * g.red_tiles + tile) * 3 + t] = sum;
+    }
+    red_dot = red_ww = red_oo = 0.f;
   }
   }  // tiles of group oi
   base += cnt;
@@ -914,16 +1045,25 @@ hipError_t launch_poly_bf16(const Batch& bt, const TileList& tl, float a, float 
                        dim3(64 * Cfg<MODE_POLY>::NW), 0, s, bt, tl, 0, a, b, c);
   return hipGetLastError();
 }
+template <class C>
+void launch_update_cfg(const Batch& bt, const TileList& tl, int iter, hipStream_t s) {
+  if (tl.fuse_tail == kLastApply)
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, C, kLastApply>), grid_of(tl), dim3(64 * C::NW), 0,
+                       s, bt, tl, iter, 0.f, 0.f, 0.f);
+  else if (tl.fuse_tail == kLastReduce)
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, C, kLastReduce>), grid_of(tl), dim3(64 * C::NW), 0,
+                       s, bt, tl, iter, 0.f, 0.f, 0.f);
+  else
+    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, C, 0>), grid_of(tl), dim3(64 * C::NW), 0, s, bt, tl,
+                       iter, 0.f, 0.f, 0.f);
+}
 hipError_t launch_update_bf16(const Batch& bt, const TileList& tl, int iter, int cfg, hipStream_t s) {
   if (cfg == kUpdCfg512)
-    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, CfgUpd512>), grid_of(tl), dim3(64 * CfgUpd512::NW),
-                       0, s, bt, tl, iter, 0.f, 0.f, 0.f);
+    launch_update_cfg<CfgUpd512>(bt, tl, iter, s);
   else if (cfg == kUpdCfg256)
-    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, CfgUpdBig>), grid_of(tl), dim3(64 * CfgUpdBig::NW),
-                       0, s, bt, tl, iter, 0.f, 0.f, 0.f);
+    launch_update_cfg<CfgUpdBig>(bt, tl, iter, s);
   else
-    hipLaunchKernelGGL((ns_bf16_kernel<MODE_UPDATE, Cfg<MODE_UPDATE>>), grid_of(tl),
-                       dim3(64 * Cfg<MODE_UPDATE>::NW), 0, s, bt, tl, iter, 0.f, 0.f, 0.f);
+    launch_update_cfg<Cfg<MODE_UPDATE>>(bt, tl, iter, s);
   return hipGetLastError();
 }
 

@@ -349,6 +349,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
   h.variant = variant & 0xff;
   const bool keller = (variant & MUON_SCALE_KELLER) != 0;
   const bool reduce = h.variant != MUON_VARIANT_MUON || stats != nullptr;
+  const bool rc_variant = h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON;
 
   Sel sel[kMaxGroups];
   int nsel = 0;
@@ -369,8 +370,9 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     Batch bt;
     std::memset(&bt, 0, sizeof(bt));
     bt.ngroups = nsel;
-    Work w_head{}, w_one{}, w_gram{}, w_upd{}, w_tail{};
+    Work w_head{}, w_one{}, w_gram{}, w_upd{}, w_tail{}, w_red{};
     w_head.ngroups = w_one.ngroups = w_gram.ngroups = w_upd.ngroups = w_tail.ngroups = nsel;
+    w_red.ngroups = nsel;
     for (int k = 0; k < nsel; ++k) {
       const muon_group& u = *sel[k].g;
       const Layout& L = sel[k].L;
@@ -425,6 +427,13 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       // so the last Newton-Schulz update applies the step to W itself (bf16
       // weights whose row length allows whole 16-byte chunks).
       m.fuse = (bf16 && !reduce && ns_steps >= 1 && (u.cols % 8) == 0) ? 1 : 0;
+      // MuonGS, MuonH and statistics need the per-matrix sums of <W,O>,
+      // ||W||^2 and ||O||^2 before W' can be written: the last update writes
+      // their per-tile partials itself (same row-length rule), so no separate
+      // reduction pass reads W and O (NorMuon and MeqMuon also need row and
+      // column sums, which the reduction pass provides).
+      m.red = (bf16 && reduce && !rc_variant && ns_steps >= 1 && (u.cols % 8) == 0) ? 1 : 0;
+      m.red_tiles = int(L.tail_tiles);   // set to the update tiles below when red
 
       const PhaseTiles pt = phase_tiles(L, dtype == MUON_DTYPE_BF16);
       w_head.tiles[k] = int(pt.head);
@@ -432,9 +441,13 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       w_gram.tiles[k] = int(pt.gram);
       w_upd.tiles[k] = int(pt.update);
       w_tail.tiles[k] = m.fuse ? 0 : int(pt.tail);
+      w_red.tiles[k] = (m.fuse || m.red) ? 0 : int(pt.tail);
     }
-    bool any_fused = false;
-    for (int k = 0; k < nsel; ++k) any_fused = any_fused || bt.g[k].fuse;
+    bool any_fused = false, any_red = false;
+    for (int k = 0; k < nsel; ++k) {
+      any_fused = any_fused || bt.g[k].fuse;
+      any_red = any_red || bt.g[k].red;
+    }
     // Symmetric products: one launch over the groups in 128x128 tiles and
     // one over the large groups in 256x256 tiles (each only if non-empty).
     TileList tl_gram{}, tl_poly{}, tl_gram_big{}, tl_poly_big{}, tl_upd{}, tl_upd_big{},
@@ -480,6 +493,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
         nu[k] = (ubig || u512) ? 0 : w_upd.tiles[k];
         nub[k] = ubig ? nb * (L.q_pad / kBigTile) : 0;
         nu5[k] = u512 ? w_upd.tiles[k] : 0;
+        if (bt.g[k].red) bt.g[k].red_tiles = int(nu5[k] ? nu5[k] : nub[k] ? nub[k] : nu[k]);
         kq[k] = bt.g[k].q_pad;
         kp[k] = bt.g[k].p_pad;
       }
@@ -492,7 +506,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       tl_upd_512 = make_tile_list(bt, nu5, kp, kBigBlocksPerCU * cpx);
     }
     hipEvent_t t0 = nullptr;
-    Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail};
+    Work* ws[] = {&w_head, &w_one, &w_gram, &w_upd, &w_tail, &w_red};
     for (Work* w : ws) {
       w->begin[0] = 0;
       for (int k = 0; k < nsel; ++k) w->begin[k + 1] = w->begin[k] + bt.g[k].count * w->tiles[k];
@@ -515,7 +529,8 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
             ((t0 = prof_start(s)),
              (st = finish_launch(launch_poly_bf16(bt, tl_poly_big, h.a, h.b, h.c, true, s), 3, s, t0))))
           return st;
-        const int fuse_tail = (it == ns_steps - 1 && any_fused) ? 1 : 0;
+        // (a call applies the step only when it reduces nothing: never both)
+        const int fuse_tail = it != ns_steps - 1 ? 0 : any_fused ? kLastApply : any_red ? kLastReduce : 0;
         const int ph = fuse_tail ? kPhaseUpdateTail : 4;
         for (int cfg = kUpdCfg128; cfg <= kUpdCfg512; ++cfg) {
           TileList tl = cfg == kUpdCfg512 ? tl_upd_512 : cfg == kUpdCfg256 ? tl_upd_big : tl_upd;
@@ -532,7 +547,10 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
     }
     if (reduce) {
       const bool rc = h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON;
-      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_reduce(bt, w_tail, bf16, ns_steps, rc, s), 5, s, t0))) return st;
+      if (w_red.begin[nsel] > 0 &&  // every group may have been reduced by its last update
+          ((t0 = prof_start(s)),
+           (st = finish_launch(launch_tail_reduce(bt, w_red, bf16, ns_steps, rc, s), 5, s, t0))))
+        return st;
       if (rc) {
         // row and column norms in blocks of kRcChunk rows or columns
         Work w_rc{};

@@ -14,6 +14,7 @@
 //                                   (bf16 path; b A + c A A on the fp32 path)
 //   head    [count][head_tiles]     per-tile partial sums of u^2
 //   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
+//                                   (red_tiles <= tail_tiles of them are used)
 //   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
 //   rc      [count][tail_tiles][128] per-tile row and column sums of O^2
 //   rcs     [count][rows + cols]    squared row and column norms of O (NorMuon, MeqMuon)
@@ -138,6 +139,9 @@ struct MatGroup {
   float decay;         // 1 - lr*wd
   float step;          // lr * s, s = 0.2*sqrt(max(rows, cols)) or max(1, rows/cols)^0.5
   int fuse;            // 1: the last update applies W' = decay W - step O itself
+  int red;             // 1: the last update writes the tail partials of <W,O>,
+                       //    ||W||^2, ||O||^2 (one triple per update tile)
+  int red_tiles;       // tail partials per matrix: update tiles when red, tail tiles otherwise
 };
 
 struct Batch {
@@ -162,9 +166,11 @@ struct TileList {
   int group[kMaxGroups];
   int ngroups;
   int blocks_per_xcd;
-  int fuse_tail;   // update launch of the last iteration: groups with fuse set
-                   // write W' instead of X'
+  int fuse_tail;   // update launch of the last iteration: kLastApply (groups with
+                   // fuse set write W' instead of X') or kLastReduce (groups with
+                   // red set also write the tail partials); 0 otherwise
 };
+enum : int { kLastApply = 1, kLastReduce = 2 };
 
 struct Hyper {
   float lr;

@@ -112,6 +112,52 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
 
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
+  const int t = threadIdx.x;
+  if (!g.trans && g.q_pad == g.cols && g.p_pad == g.rows) {
+    // No transpose and no padding: X0 = U has G's and M's layout, so the
+    // matrix is one contiguous run and a tile is 4096 consecutive elements
+    // (4 sweeps of 1024; runs of 2 / 4 KiB of G / M per sweep).  rows x cols
+    // is then a multiple of 4096 (both padded sides are multiples of 64).
+    const int64_t elems = int64_t(g.rows) * g.cols;
+    const TE* G = mat_cptr<TE>(g.G_tab, g.G, tr.m, elems);
+    float* M = mat_ptr<float>(reinterpret_cast<void* const*>(g.M_tab), reinterpret_cast<char*>(g.M),
+                              tr.m, elems);
+    TE* X = reinterpret_cast<TE*>(g.X0) + tr.m * g.x_stride;
+    const bool vec = aligned16(M) && ((reinterpret_cast<uintptr_t>(G) & (BF16 ? 7u : 15u)) == 0);
+    const int64_t base = int64_t(tr.tile) * (4 * 4 * 256) + 4 * t;
+    float u[4][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t off = base + 1024 * k;
+      if (vec) {
+        float gv[4], mv[4];
+        load4_nt(G + off, gv);
+        load4_nt(M + off, mv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mv[e] = fmaf(mu, mv[e], gv[e]);
+          u[k][e] = fmaf(mu, mv[e], gv[e]);
+        }
+        store4_nt(M + off, mv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gv = E::load(G + off + e);
+          const float mv = fmaf(mu, M[off + e], gv);
+          M[off + e] = mv;
+          u[k][e] = fmaf(mu, mv, gv);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(u[k][e], u[k][e], ss);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Vec4<BF16>::store(X + base + 1024 * k, u[k]);
+    const float tot = block_sum_256(ss, red);
+    if (t == 0) g.head_part[tr.m * g.head_tiles + tr.tile] = tot;
+    return;
+  }
   // A wide matrix (X = U, no transpose) is taken in tiles of 16 rows x 256
   // columns (row runs of 512 / 1024 bytes of G / M), or of 32 x 128 when its
   // padded row length is a multiple of 128 only; a tall one in 64 x 64
@@ -130,7 +176,6 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
                             reinterpret_cast<char*>(g.M), tr.m, elems);
   TE* X = reinterpret_cast<TE*>(g.X0) + tr.m * g.x_stride;
 
-  const int t = threadIdx.x;
   // 4 consecutive elements per thread; TC/4 threads per row, 4 sweeps
   const int tpr = TC / 4;
   const int rb = t / tpr;         // 0..15 (64x64) or 0..3 (16x256)

@@ -15,9 +15,11 @@ as many steps as take 0.25 s (at least 3): on the GPU the first ten or so
 steps run up to 20 % slower while its clocks ramp up.  Prints one JSON line:
 
   value       optimizer steps per second (whole job = one GPU)
-  roofline    the dominant kernel (the Newton-Schulz update GEMM): its
-              algorithmic flops per launch over its average launch time,
-              timed live with HIP events on the launch stream
+  roofline    the dominant kernel (the Newton-Schulz update GEMM) against
+              the roof its arithmetic intensity puts it under (HBM below the
+              ridge point, MFMA above): algorithmic bytes or flops per launch
+              over its average launch time, timed live with HIP events on the
+              launch stream; both views are given
   ns / head / tail   phase figures: NS TFLOP/s vs the bf16 MFMA peak and the
               elementwise phases' GB/s vs HBM peak
   cpu_baseline  the fp64 oracle on the host cores on a bounded sample of the
@@ -237,6 +239,24 @@ def aux_adamw(args, wl, dev, stream, muon_ms):
             "hyper": {"betas": [0.8, 0.95], "eps": 1e-10, "weight_decay": 1e-3, "lr": AUX_LR}}
 
 
+def roofline(flops, nbytes, seconds, peak_flops, peak_bw=PEAK_HBM):
+    """One launch against the roof its arithmetic intensity puts it under:
+    HBM below the ridge point (peak flops / peak bandwidth), MFMA above it;
+    both views are kept."""
+    intensity, ridge = flops / nbytes, peak_flops / peak_bw
+    mfma_view = {"achieved": flops / seconds / 1e12, "peak": peak_flops / 1e12,
+                 "unit": "TFLOP/s", "frac": flops / seconds / peak_flops,
+                 "alg_flops_per_launch": flops}
+    hbm_view = {"achieved": nbytes / seconds / 1e9, "peak": peak_bw / 1e9, "unit": "GB/s",
+                "frac": nbytes / seconds / peak_bw, "alg_bytes_per_launch": nbytes}
+    main = hbm_view if intensity < ridge else mfma_view
+    return {"bound": "hbm" if intensity < ridge else "mfma", "achieved": main["achieved"],
+            "peak": main["peak"], "unit": main["unit"], "frac": main["frac"],
+            "alg_flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
+            "flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+            "mfma_view": mfma_view, "hbm_view": hbm_view}
+
+
 def phase_profile(L, step, steps, w, es):
     """Per-launch kernel times (HIP events on the launch stream, recorded by
     the library around every launch) over `steps` more steps: the roofline
@@ -267,25 +287,17 @@ def phase_profile(L, step, steps, w, es):
     upd_iters = HP["ns_steps"] - (1 if per["update_tail"] > 0 else 0)
     if per["update"] > 0:
         upd_flops = work["update"] * upd_iters / per["update"]
-        a = upd_flops / (avg["update"] * 1e-3)
-        out["roofline"] = {
-            "kernel": "ns_update (X' = BX, B = aI + bA + cA^2)" if w.dtype == "bf16"
-                      else "ns_update (X' = aX + BX)",
-            "bound": "mfma", "achieved": a / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
-            "frac": a / peak, "traffic": measured_traffic(w.name), "avg_launch_ms": avg["update"],
-            "alg_flops_per_launch": upd_flops,
-        }
-        # The same launch against the HBM roofline: its algorithmic bytes
-        # (B and X read once, X' written once, unpadded shapes) over the same
-        # time, and the arithmetic intensity against the ridge point (dense
-        # peak / HBM peak).
+        # The launch's algorithmic bytes (B and X read once, X' written once,
+        # unpadded shapes) and its arithmetic intensity decide which roof
+        # bounds it: below the ridge point (dense peak / HBM peak) the HBM
+        # roof is the lower one (the MoE experts: short side 512), above it
+        # the MFMA roof.  Both fractions are reported.
         upd_bytes = work["update_bytes"] * upd_iters / per["update"]
-        out["roofline"]["hbm_view"] = {
-            "alg_bytes_per_launch": upd_bytes,
-            "gbps": upd_bytes / (avg["update"] * 1e-3) / 1e9,
-            "frac_of_hbm": upd_bytes / (avg["update"] * 1e-3) / PEAK_HBM,
-            "flop_per_byte": upd_flops / upd_bytes, "ridge_flop_per_byte": peak / PEAK_HBM,
-        }
+        out["roofline"] = dict(
+            {"kernel": "ns_update (X' = BX, B = aI + bA + cA^2)" if w.dtype == "bf16"
+                       else "ns_update (X' = aX + BX)"},
+            **roofline(upd_flops, upd_bytes, avg["update"] * 1e-3, peak),
+            traffic=measured_traffic(w.name), avg_launch_ms=avg["update"])
     ns_ms = per_step["gram"] + per_step["poly"] + per_step["update"] + per_step["update_tail"]
     ns_flops = HP["ns_steps"] * (work["gram"] + work["poly"] + work["update"])
     out["ns"] = {"ms_per_step": ns_ms, "tflops": ns_flops / (ns_ms * 1e-3) / 1e12,
@@ -424,7 +436,10 @@ def summary(r):
     out["unit"] = "steps/s"
     if "roofline" in r:
         out["roofline_update"] = {k: r["roofline"][k] for k in
-                                  ("achieved", "frac", "avg_launch_ms", "traffic")}
+                                  ("bound", "achieved", "unit", "frac", "avg_launch_ms",
+                                   "traffic", "flop_per_byte")}
+        out["roofline_update"]["mfma_frac"] = r["roofline"]["mfma_view"]["frac"]
+        out["roofline_update"]["hbm_frac"] = r["roofline"]["hbm_view"]["frac"]
     for k in ("ns", "head", "tail", "phase_ms_per_step"):
         if k in r:
             out[k] = r[k]

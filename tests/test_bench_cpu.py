@@ -82,3 +82,20 @@ def test_default_workload_is_the_largest_full_model():
     names = {(n, v) for n, v, _, _ in bench.EXTRAS}
     assert {("gpt160m", "muon"), ("gpt400m", "muon"), ("gpt400m", "muongs"),
             ("stress2k", "muon"), ("fp32_256x512", "muon")} <= names
+
+
+def test_roofline_picks_the_lower_roof():
+    """Below the ridge point (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B) the HBM roof
+    bounds a launch, above it the MFMA roof; the reported fraction is the
+    bounding roof's, and the MoE-1B update (216 flop/B) is HBM-bound."""
+    peak = bench.PEAK_MFMA["bf16"]
+    r = bench.roofline(216e9, 1e9, 1e-3, peak)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(1e9 / 1e-3 / bench.PEAK_HBM)
+    assert r["mfma_view"]["frac"] == pytest.approx(216e9 / 1e-3 / peak)
+    r = bench.roofline(410e9, 1e9, 1e-3, peak)
+    assert r["bound"] == "mfma" and r["frac"] == pytest.approx(410e9 / 1e-3 / peak)
+    w = bench.matrix_work(wl.WORKLOADS["moe1b"].groups, 2)
+    assert w["update"] / w["update_bytes"] < peak / bench.PEAK_HBM
+    w = bench.matrix_work(wl.WORKLOADS["gpt400m"].groups, 2)
+    assert w["update"] / w["update_bytes"] > peak / bench.PEAK_HBM

@@ -67,6 +67,14 @@
  *  Shapes   1 <= rows, cols <= MUON_MAX_DIM.  An empty batch (count == 0 or
  *           ngroups == 0) is a no-op returning MUON_OK.
  *  Concurrency  calls on different streams must use different workspaces.
+ *  Environment  MUON_DEBUG=1 synchronises the stream after every launch and
+ *           prints the failing phase's name with the HIP error (debugging
+ *           only: it breaks the no-synchronisation rule above).
+ *           MUON_TRACE=1 opens a roctx range around every Muon and AdamW
+ *           call ("muon_step", "muon_adamw_step") and one per launch, named
+ *           by its phase (see muon_profile_read), for rocprofv3
+ *           --marker-trace; the roctx library is loaded at first use, and
+ *           a message on stderr says so if it cannot be.
  */
 #ifndef MUON_MI355X_MUON_H
 #define MUON_MI355X_MUON_H

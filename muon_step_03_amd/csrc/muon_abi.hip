@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <dlfcn.h>
 #include <mutex>
 #include <vector>
 
@@ -174,6 +175,45 @@ static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == MUON_NUM_PHASES,
 constexpr int kPhaseAdamw = 8;
 constexpr int kPhaseUpdateTail = 9;  // last update launch with the step fused in
 
+// ---- optional roctx ranges (MUON_TRACE=1): one range per entry-point call
+// and one per launch, named by its phase, on the calling thread's timeline
+// (rocprofv3 --marker-trace). The roctx library is opened at run time, so
+// the library does not depend on it when tracing is off.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx* roctx() {
+  static Roctx r;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const char* e = std::getenv("MUON_TRACE");
+    if (!e || !*e || *e == '0') return;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+    if (!h) {
+      std::fprintf(stderr, "muon: MUON_TRACE is set but no roctx library loads: %s\n", dlerror());
+      return;
+    }
+    Roctx t;
+    t.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    t.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (t.push && t.pop) r = t;
+  });
+  return r.push ? &r : nullptr;
+}
+
+struct TraceRange {
+  explicit TraceRange(const char* name) : t(roctx()) {
+    if (t) t->push(name);
+  }
+  ~TraceRange() {
+    if (t) t->pop();
+  }
+  const Roctx* t;
+};
+
 // ---- optional phase timing (HIP events around each launch)
 struct ProfRecord {
   int phase;
@@ -195,8 +235,10 @@ hipEvent_t pooled_event() {
   return e;
 }
 
-// Records the start event of a launch when profiling is on.
-hipEvent_t prof_start(hipStream_t s) {
+// Opens the launch's trace range and records its start event when
+// profiling is on; finish_launch closes both.
+hipEvent_t prof_start(hipStream_t s, int phase) {
+  if (const Roctx* t = roctx()) t->push(kPhaseNames[phase]);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return nullptr;
   hipEvent_t e = pooled_event();
@@ -221,6 +263,7 @@ void prof_stop(hipEvent_t start, int phase, hipStream_t s) {
 
 int finish_launch(hipError_t e, int phase, hipStream_t s, hipEvent_t t0 = nullptr) {
   prof_stop(t0, phase, s);
+  if (const Roctx* t = roctx()) t->pop();
   if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     g_last_hip_error = int(e);
@@ -314,6 +357,7 @@ int validate_groups(const muon_group* groups, int ngroups, int dtype, double lr,
 int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, double momentum,
                double wd, int ns_steps, double a, double b, double c, int variant,
                void* workspace, size_t workspace_bytes, float* stats, void* stream) {
+  TraceRange range("muon_step");
   size_t need = 0;
   int64_t n_matrices = 0;
   int st = validate_groups(groups, ngroups, dtype, lr, momentum, wd, ns_steps, a, b, c, variant,
@@ -512,21 +556,21 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       for (int k = 0; k < nsel; ++k) w->begin[k + 1] = w->begin[k] + bt.g[k].count * w->tiles[k];
     }
 
-    if ((t0 = prof_start(s)), (st = finish_launch(launch_head(bt, w_head, bf16, h.momentum, s), 0, s, t0))) return st;
-    if ((t0 = prof_start(s)), (st = finish_launch(launch_norm_finalize(bt, w_one, s), 1, s, t0))) return st;
+    if ((t0 = prof_start(s, 0)), (st = finish_launch(launch_head(bt, w_head, bf16, h.momentum, s), 0, s, t0))) return st;
+    if ((t0 = prof_start(s, 1)), (st = finish_launch(launch_norm_finalize(bt, w_one, s), 1, s, t0))) return st;
     for (int it = 0; it < ns_steps; ++it) {
       if (bf16) {
         if (tl_gram.ngroups &&
-            ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram, it, false, s), 2, s, t0))))
+            ((t0 = prof_start(s, 2)), (st = finish_launch(launch_gram_bf16(bt, tl_gram, it, false, s), 2, s, t0))))
           return st;
         if (tl_gram_big.ngroups &&
-            ((t0 = prof_start(s)), (st = finish_launch(launch_gram_bf16(bt, tl_gram_big, it, true, s), 2, s, t0))))
+            ((t0 = prof_start(s, 2)), (st = finish_launch(launch_gram_bf16(bt, tl_gram_big, it, true, s), 2, s, t0))))
           return st;
         if (tl_poly.ngroups &&
-            ((t0 = prof_start(s)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.a, h.b, h.c, false, s), 3, s, t0))))
+            ((t0 = prof_start(s, 3)), (st = finish_launch(launch_poly_bf16(bt, tl_poly, h.a, h.b, h.c, false, s), 3, s, t0))))
           return st;
         if (tl_poly_big.ngroups &&
-            ((t0 = prof_start(s)),
+            ((t0 = prof_start(s, 3)),
              (st = finish_launch(launch_poly_bf16(bt, tl_poly_big, h.a, h.b, h.c, true, s), 3, s, t0))))
           return st;
         // (a call applies the step only when it reduces nothing: never both)
@@ -536,19 +580,19 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
           TileList tl = cfg == kUpdCfg512 ? tl_upd_512 : cfg == kUpdCfg256 ? tl_upd_big : tl_upd;
           if (!tl.ngroups) continue;
           tl.fuse_tail = fuse_tail;
-          if ((t0 = prof_start(s)), (st = finish_launch(launch_update_bf16(bt, tl, it, cfg, s), ph, s, t0)))
+          if ((t0 = prof_start(s, ph)), (st = finish_launch(launch_update_bf16(bt, tl, it, cfg, s), ph, s, t0)))
             return st;
         }
       } else {
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_gram_f32(bt, w_gram, it, s), 2, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_poly_f32(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_update_f32(bt, w_upd, it, h.a, s), 4, s, t0))) return st;
+        if ((t0 = prof_start(s, 2)), (st = finish_launch(launch_gram_f32(bt, w_gram, it, s), 2, s, t0))) return st;
+        if ((t0 = prof_start(s, 3)), (st = finish_launch(launch_poly_f32(bt, w_gram, h.b, h.c, s), 3, s, t0))) return st;
+        if ((t0 = prof_start(s, 4)), (st = finish_launch(launch_update_f32(bt, w_upd, it, h.a, s), 4, s, t0))) return st;
       }
     }
     if (reduce) {
       const bool rc = h.variant == MUON_VARIANT_NORMUON || h.variant == MUON_VARIANT_MEQMUON;
       if (w_red.begin[nsel] > 0 &&  // every group may have been reduced by its last update
-          ((t0 = prof_start(s)),
+          ((t0 = prof_start(s, 5)),
            (st = finish_launch(launch_tail_reduce(bt, w_red, bf16, ns_steps, rc, s), 5, s, t0))))
         return st;
       if (rc) {
@@ -560,12 +604,12 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
           w_rc.tiles[k] = rc_chunks(bt.g[k].rows, bt.g[k].cols);
           w_rc.begin[k + 1] = w_rc.begin[k] + bt.g[k].count * w_rc.tiles[k];
         }
-        if ((t0 = prof_start(s)), (st = finish_launch(launch_rc_sum(bt, w_rc, s), 6, s, t0))) return st;
+        if ((t0 = prof_start(s, 6)), (st = finish_launch(launch_rc_sum(bt, w_rc, s), 6, s, t0))) return st;
       }
-      if ((t0 = prof_start(s)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, rc, s), 6, s, t0))) return st;
+      if ((t0 = prof_start(s, 6)), (st = finish_launch(launch_tail_finalize(bt, w_one, h.variant, rc, s), 6, s, t0))) return st;
     }
     if (w_tail.begin[nsel] > 0 &&  // every group may have been finished by its last update
-        ((t0 = prof_start(s)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),
+        ((t0 = prof_start(s, 7)), (st = finish_launch(launch_tail_apply(bt, w_tail, bf16, h, reduce, s),
                                                     7, s, t0))))
       return st;
   }
@@ -614,6 +658,7 @@ int check_adamw_tensors(const muon_adamw_tensor* t, int64_t count, int dtype) {
 
 int run_adamw(const muon_adamw_tensor* t, int64_t count, int dtype, double beta1, double beta2,
               double eps, int64_t step, void* stream) {
+  TraceRange range("muon_adamw_step");
   if (!dtype_ok(dtype)) return MUON_ERR_UNSUPPORTED_DTYPE;
   int st = check_adamw_scalars(beta1, beta2, eps, step);
   if (st != MUON_OK) return st;
@@ -638,7 +683,7 @@ int run_adamw(const muon_adamw_tensor* t, int64_t count, int dtype, double beta1
 
   auto flush = [&]() -> int {
     if (bt.nseg == 0) return MUON_OK;
-    hipEvent_t t0 = prof_start(s);
+    hipEvent_t t0 = prof_start(s, kPhaseAdamw);
     const int r = finish_launch(launch_adamw(bt, bf16, s), kPhaseAdamw, s, t0);
     bt.nseg = 0;
     bt.begin[0] = 0;

@@ -341,3 +341,31 @@ def test_noalloc_validation(L):
     assert call([_lib.MuonGroup(1, 0, 5, None, None, None, W, G, M)]) == _lib.MUON_ERR_INVALID_SHAPE
     assert call([_lib.MuonGroup(0, 5, 5, None, None, None, None, None, None)]) == _lib.MUON_OK
     assert call([]) == _lib.MUON_OK
+
+
+def test_trace_ranges_load_roctx_and_keep_validation():
+    """MUON_TRACE=1 opens roctx ranges around each call: the library finds
+    roctx at run time, and the calls still validate and fail as without it
+    (a fresh process, since the switch is read once per process)."""
+    code = (
+        "import ctypes\n"
+        "from muon_step_03_amd import _lib\n"
+        "L = _lib.lib()\n"
+        "print(L.muon_step(None, None, None, 64, 64, 0, 0.02, 0.95, 0.1, 5, 3.4445, -4.775,"
+        " 2.0315, 0, None, 0, None, None))\n"
+        "print(L.muon_adamw_step(None, None, None, None, 16, 7, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1,"
+        " None))\n"
+        "print(int('rocprofiler-sdk-roctx' in open('/proc/self/maps').read()))\n"
+    )
+    import subprocess
+    import sys
+    out = {}
+    for trace in ("0", "1"):
+        env = dict(os.environ, MUON_TRACE=trace)
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                           text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+        assert "no roctx library" not in r.stderr
+        out[trace] = r.stdout.split()
+    assert out["1"][:2] == out["0"][:2] and "0" not in out["1"][:2]
+    assert out["0"][2] == "0" and out["1"][2] == "1"     # loaded only when tracing

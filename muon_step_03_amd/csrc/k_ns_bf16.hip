@@ -45,11 +45,11 @@
 //    read there as 16-byte rows of A (L2-resident), so the K loop carries
 //    nothing but the product.
 //  * K-contiguous operand tiles: rows of BK bf16 (4 or 8 chunks of 16 B),
-//    chunk c of row m stored at c ^ f(m), f(m) = ((m>>1) + (m>>3)) & 3 for
-//    4 chunks, (m>>1) & 7 for 8, so the fragment reads (32 consecutive rows,
-//    one chunk) do not collide in 32- or 64-bank LDS.  The swizzle is applied by choosing which
-//    global chunk each lane fetches (a direct-to-LDS load writes lane L's
-//    16 bytes at base + 16 L).
+//    chunk c of row m stored at c ^ f(m), f(m) = (m>>2) & 3 for 4 chunks,
+//    (m>>1) & 7 for 8, so the fragment reads (32 consecutive rows, one
+//    chunk) do not collide in gfx950's 64-bank LDS.  The swizzle is applied
+//    by choosing which global chunk each lane fetches (a direct-to-LDS load
+//    writes lane L's 16 bytes at base + 16 L).
 //  * The update's X operand is N-contiguous: its tile is kept as 32 K-rows
 //    of BN bf16 (chunk c of row k stored at c ^ g(k), g = {0,6,12,10}[k&3])
 //    and MFMA B fragments are read with the transposing LDS read
@@ -159,18 +159,30 @@ struct Cfg<MODE_UPDATE> {
   static constexpr int OCC = kUpdBlocksPerCU;
 };
 
-__device__ __forceinline__ int fswz(int m) { return ((m >> 1) + (m >> 3)) & 3; }
-// Row swizzle of K-contiguous tiles: 4 chunks of 16 B per row (K step 32),
-// or 8 chunks (K step 64: rows r and r+1 fill one 256-byte bank window, so
-// (r >> 1) & 7 spreads 16 consecutive rows over 16 distinct slots).
+// LDS banking measured on gfx950 (bank-conflict counters over single-pattern
+// probes): 64 banks of 4 bytes; a 16-byte read serves 16 lanes per clock
+// (lanes 0-31 and 32-63 each in two sets of four quads, split by the parity
+// of the quad index), an 8-byte read (plain or transposing) 32 lanes.
+//
+// Row swizzle of K-contiguous tiles: 4 chunks of 16 B per row (K step 32:
+// rows m, m+4, m+8, m+12 of 64 bytes fall on the same banks, so the chunk
+// index is XORed with (m >> 2) & 3), or 8 chunks (K step 64: rows r and r+1
+// fill one 256-byte bank window, so (r >> 1) & 7 spreads 16 consecutive rows
+// over 16 distinct slots).  Both are conflict-free for the fragment reads
+// (32 consecutive rows, one chunk per half wave); ((m >> 1) + (m >> 3)) & 3,
+// the first choice for 4 chunks, met 2-way conflicts.
 template <int CPR>
 __device__ __forceinline__ int rswz(int m) {
   if constexpr (CPR == 4)
-    return fswz(m);
+    return (m >> 2) & 3;
   else
     return (m >> 1) & 7;
 }
-__device__ __forceinline__ int gswz(int k) { return (0xACE0 >> ((k & 3) * 4)) & 15; }  // {0,6,12,10}
+// Chunk swizzle of the update's N-contiguous X tile (K-rows of 256 bytes, all
+// on the same banks): chunk c of K-row k is stored at c ^ {0, 6, 12, 10}[k & 3],
+// so the 4 K-rows x 64 bytes that 32 lanes of a transposing read take cover
+// the 64 banks once.
+__device__ __forceinline__ int gswz(int k) { return (0xAC60 >> ((k & 3) * 4)) & 15; }
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima).
 template <int N>

@@ -41,9 +41,10 @@
 //    LDS address is a lane's base plus an immediate: the loop body issues
 //    MFMAs, LDS reads and loads with almost no vector address arithmetic.
 //  * Epilogue: the fp32 tile is staged through LDS in 64-row passes and
-//    stored as 16-byte rows of 8 bf16; the polynomial's linear term b*A is
-//    read there as 16-byte rows of A (L2-resident), so the K loop carries
-//    nothing but the product.
+//    stored as 16-byte rows of 8 bf16 (the plain updates of the 8-wave tiles
+//    through one private window per wave instead, with no barrier between
+//    waves); the polynomial's linear term b*A is read there as 16-byte rows
+//    of A (L2-resident), so the K loop carries nothing but the product.
 //  * K-contiguous operand tiles: rows of BK bf16 (4 or 8 chunks of 16 B),
 //    chunk c of row m stored at c ^ f(m), f(m) = (m>>2) & 3 for 4 chunks,
 //    (m>>1) & 7 for 8, so the fragment reads (32 consecutive rows, one
@@ -228,6 +229,15 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Completes this wave's LDS writes before its following LDS reads of other
+// lanes' data (a wave-private exchange: no other wave takes part), and keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));  // lgkmcnt(0) only
   asm volatile("" ::: "memory");
 }
 
@@ -982,6 +992,48 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     }
   };
 
+  // Plain updates of the 8-wave tiles: each wave stages and stores its own
+  // 128x64 accumulators through a private LDS window of 32 rows, so that
+  // the epilogue needs one barrier (every wave's last K-step reads are done)
+  // and the waves then store independently.  Window pitch 68 floats; in each
+  // 8-row round a lane reads row (lane >> 2) & 7, 8-column chunk {lane bits
+  // 5, 0, 1}: both the 16-byte writes (accumulator layout) and the reads are
+  // conflict-free on gfx950, and each store instruction covers 8 rows of 128
+  // bytes.  (MoE-1B update -0.7 % against the shared 128-row passes.)
+  constexpr bool kPriv = MODE == MODE_UPDATE && LAST == 0 && C::NW == 8 && WM == 4 && WN == 2;
+  if constexpr (kPriv) {
+    constexpr int PP = 68;
+    static_assert(C::NW * 32 * PP * 4 <= S * STAGE_BYTES, "private windows");
+    block_barrier();
+    LDS_AS float* Pw = (LDS_AS float*)smem + wave * (32 * PP);
+    const int rr = (lane >> 2) & 7;
+    const int c8 = (((lane >> 5) & 1) | ((lane & 1) << 1) | (((lane >> 1) & 1) << 2)) * 8;
+#pragma unroll
+    for (int mi = 0; mi < WM; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(LDS_AS f32x4_t*)(Pw + (lane & 31) * PP + ni * 32 + 8 * g4 + 4 * (lane >> 5)) =
+              f32x4_t{acc[mi][ni][4 * g4], acc[mi][ni][4 * g4 + 1], acc[mi][ni][4 * g4 + 2],
+                      acc[mi][ni][4 * g4 + 3]};
+      wave_lds_sync();
+#pragma unroll
+      for (int rnd = 0; rnd < 4; ++rnd) {
+        const int row = rnd * 8 + rr;
+        const f32x4_t v0 = *(const LDS_AS f32x4_t*)(Pw + row * PP + c8);
+        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(Pw + row * PP + c8 + 4);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = v0[e];
+          v[e + 4] = v1[e];
+        }
+        store_nt16(out_at(i0 + wm * 32 * WM + mi * 32 + row, j0 + wn * 32 * WN + c8), pack8(v));
+      }
+      wave_lds_sync();  // the window's reads are done before the next block's writes
+    }
+  } else
 #pragma unroll
   for (int pass = 0; pass < BM / PR; ++pass) {
     // The polynomial's b*A loads are issued before the pass's staging and

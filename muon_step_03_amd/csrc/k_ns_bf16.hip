@@ -906,6 +906,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     // has fewer registers to spare, in groups of GS chunks.
     constexpr int GS = (C::NW == 8 || CHUNKS < MUON_TAIL_GS) ? CHUNKS : MUON_TAIL_GS;
     static_assert(CHUNKS % GS == 0, "chunk groups");
+    // (a tall W reads the staged tile by columns below; nothing to do by rows)
+    if (!g.trans)
 #pragma unroll
     for (int u0 = 0; u0 < CHUNKS; u0 += GS) {
       uint4 wv[GS];
@@ -939,10 +941,6 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
             else
               w_update(wp, false, v);
           }
-        } else {
-          // O is needed by columns: keep the complete values in T
-          *(LDS_AS f32x4_t*)(T + tix(row, col)) = f32x4_t{v[0], v[1], v[2], v[3]};
-          *(LDS_AS f32x4_t*)(T + tix(row, col + 4)) = f32x4_t{v[4], v[5], v[6], v[7]};
         }
       }
     }

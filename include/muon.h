@@ -266,7 +266,8 @@ int muon_adamw_step_grouped(const muon_adamw_tensor* tensors, int64_t count, int
  * 3 poly, 4 update, 5 tail_reduce, 6 tail_finalize, 7 tail_apply, 8 adamw
  * (the AdamW entry points), 9 update_tail (the last update launch when it
  * also applies the step, which plain Muon without statistics does on the
- * bf16 path: then tail_apply covers only the matrices it did not finish).
+ * bf16 path, or writes the per-tile sums of MuonGS, MuonH or statistics:
+ * then tail_reduce and tail_apply cover only the matrices it did not).
  * Returns MUON_ERR_INVALID_ARGUMENT for null arrays or nphases < 1, and
  * MUON_ERR_HIP if an event call failed.
  */

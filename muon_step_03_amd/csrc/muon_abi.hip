@@ -8,9 +8,13 @@
 //   head            M' = mu M + G, U = G + mu M', X0 = U (short side first),
 //                   per-tile sums of u^2
 //   norm_finalize   ||U||_F and 1/(||U||_F + 1e-7) per matrix
-//   ns_steps x { gram, poly, update }
-//   tail_reduce + tail_finalize   (MuonGS or stats only) <W,O>, ||W||^2, ||O||^2
-//   tail_apply      W' = (1 - lr wd) W - lr s O~
+//   ns_steps x { gram, poly, update }   (plain Muon on bf16 weights: the last
+//                   update applies the step itself; MuonGS, MuonH or stats:
+//                   it also writes per-tile <W,O>, ||W||^2, ||O||^2 partials)
+//   [tail_reduce] + tail_finalize   (variants and stats) the per-matrix sums
+//                   (tail_reduce only where the last update did not write them:
+//                   NorMuon, MeqMuon, fp32, odd row lengths)
+//   tail_apply      W' = (1 - lr wd) W - lr s O~   (where not applied already)
 // Update order: "[Deep Learning] Muon — 행렬 업데이트를 직교화하는 옵티마이저",
 // section 3 "Muon의 업데이트 순서".
 #include <algorithm>

@@ -843,3 +843,56 @@ def test_optimizer_front_end_stats_and_rebinding():
             check_against_oracle(W0[i], params[i].grad, M0[i], params[i].detach(),
                                  opt.momentum_buffers[i], variant="muongs",
                                  stats=stats[5 * row:5 * row + 5])
+
+
+_TRACE_CHILD = r'''
+import sys
+import torch
+sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, sys.argv[1] + "/tests")
+from _parity import HP
+from muon_step_03_amd import muon_step_grouped, stacked_group
+from muon_step_03_amd import workloads as wl
+shapes = [(3, 256, 640), (2, 640, 256)]
+Ws = [wl.random_matrix(c * r, k, 0.02, 1900 + i, torch.bfloat16, "cuda").view(c, r, k)
+      for i, (c, r, k) in enumerate(shapes)]
+Gs = [wl.random_matrix(c * r, k, 1e-3, 1950 + i, torch.bfloat16, "cuda").view(c, r, k)
+      for i, (c, r, k) in enumerate(shapes)]
+Ms = [torch.zeros(c, r, k, device="cuda") for c, r, k in shapes]
+for variant in ("muon", "muongs"):
+    muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Ws, Gs, Ms)], torch.bfloat16,
+                      variant=variant, **HP)
+torch.cuda.synchronize()
+torch.save({"W": [W.cpu() for W in Ws], "M": [M.cpu() for M in Ms]}, sys.argv[2])
+'''
+
+
+def test_trace_ranges_leave_results_unchanged(tmp_path):
+    """With MUON_TRACE=1 (roctx ranges around calls and launches; read once
+    per process, so the traced run is a child process) a Muon and a MuonGS
+    step give bitwise the weights and momenta of the same steps untraced."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "child.py"
+    script.write_text(_TRACE_CHILD)
+    out = tmp_path / "traced.pt"
+    env = dict(os.environ, MUON_TRACE="1")
+    r = subprocess.run([sys.executable, str(script), root, str(out)], env=env,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "no roctx library" not in r.stderr
+    traced = torch.load(str(out), weights_only=True)
+    shapes = [(3, 256, 640), (2, 640, 256)]
+    Ws = [wl.random_matrix(c * r, k, 0.02, 1900 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(shapes)]
+    Gs = [wl.random_matrix(c * r, k, 1e-3, 1950 + i, torch.bfloat16, DEV).view(c, r, k)
+          for i, (c, r, k) in enumerate(shapes)]
+    Ms = [torch.zeros(c, r, k, device=DEV) for c, r, k in shapes]
+    for variant in ("muon", "muongs"):
+        muon_step_grouped([stacked_group(W, G, M) for W, G, M in zip(Ws, Gs, Ms)],
+                          torch.bfloat16, variant=variant, **HP)
+    torch.cuda.synchronize()
+    for x, y in zip(Ws + Ms, traced["W"] + traced["M"]):
+        assert torch.equal(x.cpu(), y)

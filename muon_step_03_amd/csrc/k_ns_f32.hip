@@ -10,14 +10,20 @@
 // 진단과 처방 ... Muon 전환 판단", section "Muon head의 실체는 하이브리드
 // 옵티마이저다").
 //
-// Block tile 64x64, K step 16, 256 threads each owning a 4x4 output patch.
+// Block tile 64x64, K step 32, 1024 threads in four groups of 256: group g
+// multiplies the g-th quarter of the K steps (each thread a 4x4 output
+// patch, two LDS stages per group, the next K step's operands loaded into
+// registers while the current one is multiplied), and the four partial
+// tiles are summed through LDS in group order.  Small float32 matrices give
+// these launches few blocks, so a tile's chain of K steps sets their time:
+// the split shortens it four-fold (bitwise reproducible: a fixed order).
 #include "muon_internal.h"
 
 namespace muon {
 namespace {
 
 constexpr int TB = kF32Tile;  // 64
-constexpr int BKF = 16;
+constexpr int BKF = 32;
 
 enum { MODE_GRAM = 0, MODE_POLY = 1, MODE_UPDATE = 2 };
 
@@ -29,11 +35,13 @@ __device__ __forceinline__ void tri_decode(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
+constexpr int KGROUPS = 4;
+
 template <int MODE>
-__global__ __launch_bounds__(256) void ns_f32_kernel(Batch bt, Work wk, int iter, float c1,
-                                                     float c2) {
-  __shared__ __attribute__((aligned(16))) float As[BKF][TB + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[BKF][TB + 4];
+__global__ __launch_bounds__(256 * KGROUPS) void ns_f32_kernel(Batch bt, Work wk, int iter,
+                                                               float c1, float c2) {
+  __shared__ __attribute__((aligned(16))) float As[KGROUPS][2][BKF][TB + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[KGROUPS][2][BKF][TB + 4];
 
   const int64_t bid = blockIdx.x;
   const int gi = find_group(wk, bid);
@@ -80,7 +88,8 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(Batch bt, Work wk, int iter
     K = g.p_pad;
   }
 
-  const int t = threadIdx.x;
+  const int kg = int(threadIdx.x) >> 8;   // K group
+  const int t = int(threadIdx.x) & 255;
   const int tm = t >> 4, tn = t & 15;
   float acc[4][4];
 #pragma unroll
@@ -88,32 +97,56 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(Batch bt, Work wk, int iter
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
 
-  for (int k0 = 0; k0 < K; k0 += BKF) {
-    {
-      const int row = t >> 2, kq = (t & 3) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(Pa + row * lda + k0 + kq);
-      As[kq + 0][row] = v.x;
-      As[kq + 1][row] = v.y;
-      As[kq + 2][row] = v.z;
-      As[kq + 3][row] = v.w;
-      if (MODE != MODE_UPDATE) {
-        const float4 w = *reinterpret_cast<const float4*>(Pb + row * ldb + k0 + kq);
-        Bs[kq + 0][row] = w.x;
-        Bs[kq + 1][row] = w.y;
-        Bs[kq + 2][row] = w.z;
-        Bs[kq + 3][row] = w.w;
-      }
+  // Operand loads of one K step: the K-contiguous tiles (A, and the Gram's
+  // and polynomial's B) as 64 rows x 32 k, two float4 per thread, stored
+  // transposed (k-major) in LDS; the update's X tile as 32 k-rows x 64.
+  const int lrow = t >> 2, lkq = (t & 3) * 8;
+  const int lkk = t >> 3, lnq = (t & 7) * 8;
+  float4 ra0, ra1, rb0, rb1;
+  auto gload = [&](int k0) {
+    const float* pa = Pa + lrow * lda + k0 + lkq;
+    ra0 = *reinterpret_cast<const float4*>(pa);
+    ra1 = *reinterpret_cast<const float4*>(pa + 4);
+    if (MODE != MODE_UPDATE) {
+      const float* pb = Pb + lrow * ldb + k0 + lkq;
+      rb0 = *reinterpret_cast<const float4*>(pb);
+      rb1 = *reinterpret_cast<const float4*>(pb + 4);
+    } else {
+      const float* pb = Pb + (k0 + lkk) * ldb + lnq;
+      rb0 = *reinterpret_cast<const float4*>(pb);
+      rb1 = *reinterpret_cast<const float4*>(pb + 4);
     }
-    if (MODE == MODE_UPDATE) {
-      const int kk = t >> 4, nq = (t & 15) * 4;
-      *reinterpret_cast<float4*>(&Bs[kk][nq]) =
-          *reinterpret_cast<const float4*>(Pb + (k0 + kk) * ldb + nq);
-    }
-    __syncthreads();
+  };
+  auto sstore = [&](int buf) {
+    const float a8[8] = {ra0.x, ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w};
 #pragma unroll
+    for (int j = 0; j < 8; ++j) As[kg][buf][lkq + j][lrow] = a8[j];
+    if (MODE != MODE_UPDATE) {
+      const float b8[8] = {rb0.x, rb0.y, rb0.z, rb0.w, rb1.x, rb1.y, rb1.z, rb1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Bs[kg][buf][lkq + j][lrow] = b8[j];
+    } else {
+      *reinterpret_cast<float4*>(&Bs[kg][buf][lkk][lnq]) = rb0;
+      *reinterpret_cast<float4*>(&Bs[kg][buf][lkk][lnq + 4]) = rb1;
+    }
+  };
+  // this group's K steps: [s0, s1) of the K / BKF steps (possibly none)
+  const int nsteps = K / BKF;
+  const int s0 = nsteps * kg / KGROUPS, s1 = nsteps * (kg + 1) / KGROUPS;
+  if (s0 < s1) {
+    gload(s0 * BKF);
+    sstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int st = s0; st < s1; ++st) {
+    const int k0 = st * BKF;
+    const bool more = st + 1 < s1;
+    if (more) gload(k0 + BKF);   // in flight during this step's products
+#pragma unroll 8
     for (int k = 0; k < BKF; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(&As[k][tm * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&Bs[k][tn * 4]);
+      const float4 a = *reinterpret_cast<const float4*>(&As[kg][buf][k][tm * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&Bs[kg][buf][k][tn * 4]);
       const float av[4] = {a.x, a.y, a.z, a.w};
       const float bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -121,8 +154,38 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(Batch bt, Work wk, int iter
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
     }
+    // the other stage was last read before the previous barrier
+    if (more) sstore(buf ^ 1);
+    // (groups run different step counts: a group-local barrier would do, but
+    // the block barrier keeps the code plain; a group past its last step
+    // still passes it)
     __syncthreads();
+    buf ^= 1;
   }
+  // groups with fewer steps meet the others' remaining barriers here
+  for (int st = s1 - s0; st < (nsteps + KGROUPS - 1) / KGROUPS; ++st) __syncthreads();
+
+  // The four partial tiles, summed in group order (As is free again).
+  float* R = &As[0][0][0][0];
+  static_assert(sizeof(As) >= sizeof(float) * (KGROUPS - 1) * TB * TB, "partials fit");
+  if (kg > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<float4*>(&R[((kg - 1) * TB + tm * 4 + r) * TB + tn * 4]) =
+          make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+  }
+  __syncthreads();
+  if (kg > 0) return;
+#pragma unroll
+  for (int q = 0; q < KGROUPS - 1; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 v = *reinterpret_cast<const float4*>(&R[(q * TB + tm * 4 + r) * TB + tn * 4]);
+      acc[r][0] += v.x;
+      acc[r][1] += v.y;
+      acc[r][2] += v.z;
+      acc[r][3] += v.w;
+    }
 
   const float* sc = g.scal + m * kScal;
   float alpha = 1.f, beta = 0.f;
@@ -162,15 +225,15 @@ inline dim3 grid_of(const Work& wk) { return dim3(unsigned(wk.begin[wk.ngroups])
 }  // namespace
 
 hipError_t launch_gram_f32(const Batch& bt, const Work& wk, int iter, hipStream_t s) {
-  hipLaunchKernelGGL(ns_f32_kernel<MODE_GRAM>, grid_of(wk), dim3(256), 0, s, bt, wk, iter, 0.f, 0.f);
+  hipLaunchKernelGGL(ns_f32_kernel<MODE_GRAM>, grid_of(wk), dim3(256 * KGROUPS), 0, s, bt, wk, iter, 0.f, 0.f);
   return hipGetLastError();
 }
 hipError_t launch_poly_f32(const Batch& bt, const Work& wk, float b, float c, hipStream_t s) {
-  hipLaunchKernelGGL(ns_f32_kernel<MODE_POLY>, grid_of(wk), dim3(256), 0, s, bt, wk, 0, b, c);
+  hipLaunchKernelGGL(ns_f32_kernel<MODE_POLY>, grid_of(wk), dim3(256 * KGROUPS), 0, s, bt, wk, 0, b, c);
   return hipGetLastError();
 }
 hipError_t launch_update_f32(const Batch& bt, const Work& wk, int iter, float a, hipStream_t s) {
-  hipLaunchKernelGGL(ns_f32_kernel<MODE_UPDATE>, grid_of(wk), dim3(256), 0, s, bt, wk, iter, a, 0.f);
+  hipLaunchKernelGGL(ns_f32_kernel<MODE_UPDATE>, grid_of(wk), dim3(256 * KGROUPS), 0, s, bt, wk, iter, a, 0.f);
   return hipGetLastError();
 }
 

@@ -369,6 +369,35 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   static_assert(C::WGM * C::WGN == C::NW && BM % 64 == 0, "wave grid; 64-row epilogue passes");
+  // 32x32 accumulator blocks of a wave: tile row block rblk(mi), column
+  // block cblk(ni).  The 256x256 symmetric tiles (8 x 8 blocks, waves of 4
+  // row blocks by 2 column blocks) take rows {0,1,5,6} (wm 0) or {2,3,4,7}
+  // (wm 1) and columns {wn, 7-wn}: on a diagonal tile, whose 28 blocks
+  // above the diagonal are not computed (their values are the transposes of
+  // the blocks below it), every wave of the first group then has 4 blocks
+  // to compute and every wave of the second 5, against 8 for the
+  // consecutive rows and columns of the other tiles (where the two
+  // assignments do the same work).
+  constexpr bool kBal = MODE != MODE_UPDATE && C::NW == 8 && C::WGM == 2 && C::WGN == 4 &&
+                        WM == 4 && WN == 2;
+  auto rblk = [&](int mi) -> int {
+    if constexpr (kBal) return mi < 2 ? 2 * wm + mi : (mi == 2 ? 5 - wm : 6 + wm);
+    else return wm * WM + mi;
+  };
+  auto cblk = [&](int ni) -> int {
+    if constexpr (kBal) return ni == 0 ? wn : 7 - wn;
+    else return wn * WN + ni;
+  };
+  // Blocks (mi, ni) of this wave strictly above a diagonal tile's diagonal
+  // (bit mi * WN + ni): not computed there.
+  uint32_t upper = 0;
+  if constexpr (kBal) {
+#pragma unroll
+    for (int mi = 0; mi < WM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < WN; ++ni)
+        if (rblk(mi) < cblk(ni)) upper |= 1u << (mi * WN + ni);
+  }
   const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
 
   // LDS holds the A tiles of all stages, then the B tiles (stage s of A at
@@ -440,25 +469,30 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi)
-      af[mi] = lds_frag_rows<BK>(sA, wm * 32 * WM + mi * 32 + (lane & 31), ch);
+      af[mi] = lds_frag_rows<BK>(sA, rblk(mi) * 32 + (lane & 31), ch);
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni) {
       if (MODE == MODE_UPDATE)
         bfr[ni] = lds_frag_xT<BN>(sB, ks * 16, wn * 32 * WN + ni * 32, lane);
       else
-        bfr[ni] = lds_frag_rows<BK>(sB, wn * 32 * WN + ni * 32 + (lane & 31), ch);
+        bfr[ni] = lds_frag_rows<BK>(sB, cblk(ni) * 32 + (lane & 31), ch);
     }
   };
   // The B fragment goes in the MFMA's first operand slot: the accumulator
   // then holds the tile transposed, so that lane l, register 4g + jj is row
   // l%32, column 8g + 4(l/32) + jj of its 32x32 block: 4 consecutive columns
   // of one row per 4 registers (16-byte LDS writes in the epilogue).
-  auto mfmas = [&](const bf16x8_t (&af)[WM], const bf16x8_t (&bfr)[WN]) {
+  // On a diagonal tile (dgc) of the balanced layout the blocks above the
+  // diagonal are skipped (a wave-uniform branch).
+  auto mfmas = [&](auto dgc, const bf16x8_t (&af)[WM], const bf16x8_t (&bfr)[WN]) {
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < WN; ++ni)
+      for (int ni = 0; ni < WN; ++ni) {
+        if constexpr (kBal && decltype(dgc)::value)
+          if ((upper >> (mi * WN + ni)) & 1u) continue;
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+      }
   };
   // Waits until the loads of `stage` are done, given that the last stage
   // issued so far is `issued` (capped at nk-1): exactly the loads of the
@@ -513,8 +547,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     if (kt + S - 1 < nk) issue(std::integral_constant<int, (J + S - 1) % S>{}, dg, kt + S - 1);
     if (late && kt + 1 < nk) wait_stage(dg, kt + 1, kt + S - 1);
     block_barrier();
-    mfmas(a0, b0);
-    mfmas(a1, b1);
+    mfmas(dg, a0, b0);
+    mfmas(dg, a1, b1);
     if (!late && kt + 1 < nk) wait_stage(dg, kt + 1, kt + S - 1);
     block_barrier();
   };
@@ -536,12 +570,12 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   auto step = [&](auto bufc, int kt) {
     constexpr int J = decltype(bufc)::value;
     load_frags(bufc, dg, 1, a1, b1);
-    mfmas(a0, b0);
+    mfmas(dg, a0, b0);
     if constexpr (KS == 4) {
       load_frags(bufc, dg, 2, a0, b0);
-      mfmas(a1, b1);
+      mfmas(dg, a1, b1);
       load_frags(bufc, dg, 3, a1, b1);
-      mfmas(a0, b0);
+      mfmas(dg, a0, b0);
     }
     if (kt + 1 < nk) {
       wait_stage(dg, kt + 1, kt + S - 1);  // steps up to kt+S-1 issued so far
@@ -549,7 +583,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       if (kt + S < nk) issue(bufc, dg, kt + S);
       load_frags(std::integral_constant<int, (J + 1) % S>{}, dg, 0, a0, b0);
     }
-    mfmas(a1, b1);
+    mfmas(dg, a1, b1);
   };
   for (int kt = 0; kt < nk; kt += S) {
     step(std::integral_constant<int, 0>{}, kt);
@@ -581,6 +615,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     alpha = iter == 0 ? sc[SC_INV] : 1.f;
   }
   const bool mirror = (MODE != MODE_UPDATE) && (ti != tj);
+  // A diagonal tile of the balanced layout computed only the blocks on and
+  // below the diagonal: the direct pass writes those, the mirrored pass the
+  // transposes of the blocks strictly below it.  (Chunks of 8 columns, or 8
+  // rows, never straddle a 32x32 block.)
+  const bool dtri = kBal && ti == tj;
   // Final values in fp32, before one rounding: Gram alpha*(X X^T),
   // polynomial c*(A A) + b*A + a*I, update alpha*(B X).
 #pragma unroll
@@ -616,14 +655,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   auto stage = [&](int pass) {
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi) {
-      const int blk = wm * WM + mi;
+      const int blk = rblk(mi);
       if (blk / (PR / 32) != pass) continue;
       const int row = (blk % (PR / 32)) * 32 + (lane & 31);
 #pragma unroll
       for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = wn * 32 * WN + ni * 32 + 8 * g4 + 4 * (lane >> 5);
+          const int col = cblk(ni) * 32 + 8 * g4 + 4 * (lane >> 5);
           *(LDS_AS f32x4_t*)(T + tix(row, col)) =
               f32x4_t{acc[mi][ni][4 * g4], acc[mi][ni][4 * g4 + 1], acc[mi][ni][4 * g4 + 2],
                       acc[mi][ni][4 * g4 + 3]};
@@ -657,14 +696,14 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   auto stage_t = [&](int pass) {
 #pragma unroll
     for (int mi = 0; mi < WM; ++mi) {
-      const int blk = wm * WM + mi;
+      const int blk = rblk(mi);
       if ((blk >> 1) != pass) continue;
       const int row = (blk & 1) * 32 + (lane & 31);
 #pragma unroll
       for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int col = wn * 32 * WN + ni * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = cblk(ni) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           T[col * TPT + row] = acc[mi][ni][r];
         }
     }
@@ -700,7 +739,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
         const int row = q / CPR, col = (q % CPR) * 8;
         lin[u] = *reinterpret_cast<const uint4*>(Lin + (i0 + PR * pass + row) * ldc + j0 + col);
       }
-      if (mirror) {
+      if (mirror || dtri) {
 #pragma unroll
         for (int u = 0; u < MCH; ++u) {
           int c, r8;
@@ -716,6 +755,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     for (int u = 0; u < CHUNKS; ++u) {
       const int q = t + NT * u;
       const int row = q / CPR, col = (q % CPR) * 8;
+      if (dtri && (PR * pass + row) / 32 < col / 32) continue;
       float v[8];
       const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + tix(row, col));
       const f32x4_t v1 = *(const LDS_AS f32x4_t*)(T + tix(row, col + 4));
@@ -739,6 +779,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     for (int u = 0; u < MCH; ++u) {
       int c, r8;
       mirror_pos(t + NT * u, c, r8);
+      if (dtri && (PR * pass + r8) / 32 <= c / 32) continue;
       float v[8];
       if constexpr (kStageT) {
         const f32x4_t v0 = *(const LDS_AS f32x4_t*)(T + c * TPT + r8);
@@ -1059,7 +1100,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
       if (!kEarlyLin) load_lin(pass, lin, lin_m);
       finish(pass, lin, lin_m);
       if constexpr (MODE != MODE_UPDATE) {
-        if (mirror) {
+        if (mirror || dtri) {
           if constexpr (kStageT) {
             block_barrier();  // the row reads of T are done
             stage_t(pass);

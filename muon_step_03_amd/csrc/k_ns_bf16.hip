@@ -7,7 +7,7 @@
 //                             computed, each written to both triangles
 //   B = a*I + b*A + c*A A^T   A is symmetric, so A A = A A^T: the same
 //                             symmetric form with K = p; b*A and a*I are
-//                             added in the fp32 epilogue
+//                             added in fp32 before the one rounding
 //   X' = B X                  full p x q output, a plain product
 // which is X_k = aX + b(XX^T)X + c(XX^T)^2 X = (aI + bA + cA^2) X of "[논문
 // AI 리뷰] MUON IS SCALABLE FOR LLM TRAINING TECHNICAL REPORT", section 2.
@@ -43,8 +43,10 @@
 //  * Epilogue: the fp32 tile is staged through LDS in 64-row passes and
 //    stored as 16-byte rows of 8 bf16 (the plain updates of the 8-wave tiles
 //    through one private window per wave instead, with no barrier between
-//    waves); the polynomial's linear term b*A is read there as 16-byte rows
-//    of A (L2-resident), so the K loop carries nothing but the product.
+//    waves).  The polynomial's linear term b*A: the 128x128 tiles pick it
+//    from the K step whose columns are the tile's own (8-byte LDS reads at
+//    the accumulator positions, added before staging); the 256x256 tiles
+//    read it in the epilogue as 16-byte rows of A.
 //  * K-contiguous operand tiles: rows of BK bf16 (4 or 8 chunks of 16 B),
 //    chunk c of row m stored at c ^ f(m), f(m) = (m>>2) & 3 for 4 chunks,
 //    (m>>1) & 7 for 8, so the fragment reads (32 consecutive rows, one
@@ -74,6 +76,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int WAVE_BYTES = 1024;    // bytes one direct-to-LDS instruction moves
@@ -461,6 +464,42 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
+  // The 128x128 polynomial takes its linear term b*A from the K loop: the
+  // tile's columns j0 .. j0+127 are K columns of its own operand rows
+  // i0 .., and a wave's 64 columns are exactly K step klin, so during that
+  // step each lane reads from the A stage the 4 consecutive elements of A
+  // at each group of 4 accumulator registers (one 8-byte LDS read each).
+  // No A tile is read again from memory in the epilogue.
+  constexpr bool kLinK = MODE == MODE_POLY && C::NW == 4 && BM == BN && BK == 32 * WN;
+  u32x2_t linr[kLinK ? WM : 1][kLinK ? WN : 1][4];
+  const int klin = kLinK ? (j0 + wn * 32 * WN) / BK : -1;
+  if constexpr (kLinK) {
+#pragma unroll
+    for (int mi = 0; mi < WM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) linr[mi][ni][g4] = u32x2_t{0u, 0u};  // K step past p: zeros
+  }
+  auto read_lin = [&](auto bufc) {
+    if constexpr (kLinK) {
+      constexpr int J = decltype(bufc)::value;
+      const LDS_AS char* sA = smem + J * A_BYTES;
+#pragma unroll
+      for (int mi = 0; mi < WM; ++mi) {
+        const int row = rblk(mi) * 32 + (lane & 31);
+#pragma unroll
+        for (int ni = 0; ni < WN; ++ni)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int kc = ni * 32 + 8 * g4 + 4 * (lane >> 5);  // K column in the step
+            linr[mi][ni][g4] = *reinterpret_cast<const LDS_AS u32x2_t*>(
+                sA + row * (BK * 2) + (((kc >> 3) ^ rswz<CPK>(row)) << 4) + (kc & 7) * 2);
+          }
+      }
+    }
+  };
+
   // Fragments of one 16-deep K sub-step of stage buffer J.
   auto load_frags = [&](auto bufc, auto diagc, int ks, bf16x8_t (&af)[WM], bf16x8_t (&bfr)[WN]) {
     constexpr int J = decltype(bufc)::value;
@@ -569,6 +608,7 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   load_frags(std::integral_constant<int, 0>{}, dg, 0, a0, b0);
   auto step = [&](auto bufc, int kt) {
     constexpr int J = decltype(bufc)::value;
+    if (kLinK && kt == klin) read_lin(bufc);
     load_frags(bufc, dg, 1, a1, b1);
     mfmas(dg, a0, b0);
     if constexpr (KS == 4) {
@@ -627,7 +667,15 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
 #pragma unroll
     for (int ni = 0; ni < WN; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= (MODE == MODE_POLY ? cc : alpha);
+      for (int r = 0; r < 16; ++r) {
+        acc[mi][ni][r] *= (MODE == MODE_POLY ? cc : alpha);
+        if constexpr (kLinK) {
+          const u32x2_t w = linr[mi][ni][r >> 2];
+          const uint32_t h = (r & 2) ? w[1] : w[0];
+          const float a = __uint_as_float((r & 1) ? (h & 0xffff0000u) : (h << 16));
+          acc[mi][ni][r] = fmaf(cb, a, acc[mi][ni][r]);
+        }
+      }
   // fp32 staging row pitch (floats): 4 mod 64 banks, so the 16-byte writes of
   // 16 lanes (16 consecutive rows, one column) cover all banks once.  Passes
   // of PR rows: 64, or 128 for the 512-row tiles (the same bytes per pass).
@@ -714,10 +762,10 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     for (int e = 0; e < 4; ++e) w[e] = f2bf2(v[2 * e], v[2 * e + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   };
-  // The polynomial's linear term b*A at the output positions, read as
-  // 16-byte rows of A (L2-resident: its K steps just streamed through).  A
-  // is symmetric, so a mirrored chunk's term is again a row segment of A.
-  constexpr bool kLin = MODE == MODE_POLY;
+  // The 256x256 polynomial's linear term b*A at the output positions, read
+  // as 16-byte rows of A in the epilogue.  A is symmetric, so a mirrored
+  // chunk's term is again a row segment of A.
+  constexpr bool kLin = MODE == MODE_POLY && !kLinK;
   constexpr int MCH = BN * (PR / 8) / NT;    // mirrored chunks per thread per pass
   const uint16_t* Lin = Am;
   const float lin_coef = cb;
@@ -1075,12 +1123,11 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
   } else
 #pragma unroll
   for (int pass = 0; pass < BM / PR; ++pass) {
-    // The polynomial's b*A loads are issued before the pass's staging and
-    // barriers where registers allow (64x64 wave tiles, and the 256x256
-    // tiles, whose one block per CU has no other block to hide their latency
-    // behind), after the staging otherwise.
+    // The 256x256 polynomial's b*A loads are issued before the pass's
+    // staging and barriers: its one block per CU has no other block to hide
+    // their latency behind.
     uint4 lin[kLin ? CHUNKS : 1], lin_m[kLin ? MCH : 1];
-    constexpr bool kEarlyLin = kLin && (WM * WN <= 4 || C::NW == 8);
+    constexpr bool kEarlyLin = kLin;
     if (kEarlyLin && !fuse) load_lin(pass, lin, lin_m);
     block_barrier();  // stage buffers (pass 0) / the previous pass's T no longer read
     stage(pass);

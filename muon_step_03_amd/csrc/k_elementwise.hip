@@ -102,13 +102,16 @@ __device__ __forceinline__ void store4_nt(float* p, const float* v) {
 // ------------------------------------------------------------------- head
 // M' = mu*M + G, U = G + mu*M' on one 64x64 tile of X (X = U, or U^T for a
 // tall matrix); writes M' in place, U (rounded to X's type) into X0 with
-// zeros in the padding, and the tile's sum of u^2 (fp32, unrounded u).
+// zeros in the padding, and the tile's sum of u^2 (unrounded u, summed in
+// fp64: the total then hardly depends on how the matrix is cut into tiles,
+// which differs between a matrix and its transpose, so that the step of W^T
+// is the transpose of W's bit for bit).
 template <bool BF16>
 __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) {
   using E = Elem<BF16>;
   using TE = typename E::T;
   __shared__ float S[T][T + 1];
-  __shared__ float red[4];
+  __shared__ double red[4];
 
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
     const bool vec = aligned16(M) && ((reinterpret_cast<uintptr_t>(G) & (BF16 ? 7u : 15u)) == 0);
     const int64_t base = int64_t(tr.tile) * (4 * 4 * 256) + 4 * t;
     float u[4][4];
-    float ss = 0.f;
+    double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int64_t off = base + 1024 * k;
@@ -150,11 +153,11 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
         }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ss = fmaf(u[k][e], u[k][e], ss);
+      for (int e = 0; e < 4; ++e) ss = fma(double(u[k][e]), double(u[k][e]), ss);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) Vec4<BF16>::store(X + base + 1024 * k, u[k]);
-    const float tot = block_sum_256(ss, red);
+    const double tot = block_sum_256(ss, red);
     if (t == 0) g.head_part[tr.m * g.head_tiles + tr.tile] = tot;
     return;
   }
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
                    ((reinterpret_cast<uintptr_t>(G) & (BF16 ? 7u : 15u)) == 0);
 
   float u[4][4];
-  float ss = 0.f;
+  double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = sr0 + rb + rstep * k;
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ss = fmaf(u[k][e], u[k][e], ss);
+    for (int e = 0; e < 4; ++e) ss = fma(double(u[k][e]), double(u[k][e]), ss);
   }
 
   if (!g.trans) {
@@ -239,26 +242,27 @@ __global__ __launch_bounds__(256) void head_kernel(Batch bt, Work wk, float mu) 
     }
   }
 
-  const float tot = block_sum_256(ss, red);
+  const double tot = block_sum_256(ss, red);
   if (t == 0) g.head_part[tr.m * g.head_tiles + tr.tile] = tot;
 }
 
-// ||U||_F from the head partials of one matrix (one block per matrix, fixed
-// summation order).
+// ||U||_F and 1/(||U||_F + 1e-7) from the head partials of one matrix (one
+// block per matrix, fixed summation order, fp64 until the two scalars are
+// rounded to fp32).
 __global__ __launch_bounds__(256) void norm_finalize_kernel(Batch bt, Work wk) {
-  __shared__ float red[4];
+  __shared__ double red[4];
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
-  const float* part = g.head_part + tr.m * g.head_tiles;
-  float s = 0.f;
+  const double* part = g.head_part + tr.m * g.head_tiles;
+  double s = 0.0;
   for (int i = threadIdx.x; i < g.head_tiles; i += 256) s += part[i];
   s = block_sum_256(s, red);
   if (threadIdx.x == 0) {
-    const float n = sqrtf(s);
+    const double n = sqrt(s);
     float* sc = g.scal + tr.m * kScal;
-    sc[SC_NORM] = n;
-    sc[SC_INV] = 1.0f / (n + kEps);
-    if (g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 0] = n;
+    sc[SC_NORM] = float(n);
+    sc[SC_INV] = float(1.0 / (n + double(kEpsNorm)));
+    if (g.stats) g.stats[tr.m * MUON_STATS_PER_MATRIX + 0] = float(n);
   }
 }
 

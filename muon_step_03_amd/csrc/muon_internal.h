@@ -12,7 +12,7 @@
 //                                   edge masking.
 //   A, B    [count][p_pad][p_pad]   Gram matrix X X^T and polynomial a I + b A + c A A
 //                                   (bf16 path; b A + c A A on the fp32 path)
-//   head    [count][head_tiles]     per-tile partial sums of u^2
+//   head    [count][head_tiles]     per-tile partial sums of u^2 (fp64)
 //   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
 //                                   (red_tiles <= tail_tiles of them are used)
 //   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
@@ -91,7 +91,7 @@ constexpr int kUpdTileN = MUON_UPD_TILE_N;  // update: columns (along q)
 constexpr int kBf16PadP = kSyrkTile > kUpdTileM ? kSyrkTile : kUpdTileM;
 constexpr int kBf16PadQ = kUpdTileN > kSyrkTile ? kUpdTileN : kSyrkTile;
 constexpr int kF32Tile = 64;       // fp32 GEMM block tile edge
-constexpr float kEps = 1e-7f;      // added to ||U||_F before dividing
+constexpr double kEpsNorm = 1e-7;  // added to ||U||_F before dividing
 
 // Per-matrix scalar slots.
 enum : int {
@@ -129,7 +129,7 @@ struct MatGroup {
   char* B;
   int64_t x_stride;    // elements between matrices in X0/X1
   int64_t a_stride;    // elements between matrices in A/B
-  float* head_part;
+  double* head_part;   // [count][head_tiles]: per-tile sums of u^2 (fp64)
   float* tail_part;
   float* rc_part;      // [count][tail_tiles][128]: per-tile row and column sums of O^2
   float* rc_norm2;     // [count][rows + cols]: squared row, then column norms of O
@@ -228,8 +228,9 @@ struct Elem<false> {
 };
 
 // Sum of v over the 256-thread block, in a fixed order (deterministic).
-// `red` must hold 4 floats of LDS.  Result valid in every thread.
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
+// `red` must hold 4 values of LDS.  Result valid in every thread.
+template <typename F>
+__device__ __forceinline__ F block_sum_256(F v, F* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   const int wave = threadIdx.x >> 6;

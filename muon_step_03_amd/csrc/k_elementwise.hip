@@ -362,7 +362,8 @@ __device__ __forceinline__ void load_w_tile(const MatGroup& g, const typename El
 }
 
 // Block sums of three values with one pair of barriers.
-__device__ __forceinline__ void block_sum3_256(float& a, float& b, float& c, float* red) {
+template <typename F>
+__device__ __forceinline__ void block_sum3_256(F& a, F& b, F& c, F* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     a += __shfl_xor(a, off, 64);
@@ -388,7 +389,7 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int ns_steps, int rc) {
   using TE = typename Elem<BF16>::T;
   __shared__ float S[T][T + 1];
-  __shared__ float red[12];
+  __shared__ double red[12];
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
   const TailTile tt = tail_tile(g, tr.tile, !rc);
@@ -403,19 +404,21 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(Batch bt, Work wk, int
   // (the apply, which reads them again, is no slower for it)
   load_w_tile<BF16, true>(g, W, tt, w, valid);
   load_o_tile<BF16, true>(g, X, tt, S, o);
-  float dot = 0.f, ww = 0.f, oo = 0.f;
+  // (sums in fp64, as the head's: W's and W^T's tiles then give the same
+  // totals to the last bit of their fp32 rounding)
+  double dot = 0.0, ww = 0.0, oo = 0.0;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float ov = valid[k][e] ? o[k][e] * oscale : 0.f;
-      dot = fmaf(w[k][e], ov, dot);
-      ww = fmaf(w[k][e], w[k][e], ww);
-      oo = fmaf(ov, ov, oo);
+      const double wv = w[k][e], ov = valid[k][e] ? o[k][e] * oscale : 0.f;
+      dot = fma(wv, ov, dot);
+      ww = fma(wv, wv, ww);
+      oo = fma(ov, ov, oo);
     }
   block_sum3_256(dot, ww, oo, red);
   if (threadIdx.x == 0) {
-    float* p = g.tail_part + (tr.m * g.red_tiles + tr.tile) * 3;
+    double* p = g.tail_part + (tr.m * g.red_tiles + tr.tile) * 3;
     p[0] = dot;
     p[1] = ww;
     p[2] = oo;
@@ -552,11 +555,11 @@ __device__ void rc_merge(const MatGroup& g, int64_t m, int variant) {
 // optional stats; with rc (NorMuon, MeqMuon) also the equalisation's
 // direction and target (rc_sum_kernel ran before).
 __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, int variant, int rc) {
-  __shared__ float red[12];
+  __shared__ double red[12];
   const TileRef tr = decode(bt, wk, blockIdx.x);
   const MatGroup& g = *tr.g;
-  const float* part = g.tail_part + tr.m * g.red_tiles * 3;
-  float dot = 0.f, ww = 0.f, oo = 0.f;
+  const double* part = g.tail_part + tr.m * g.red_tiles * 3;
+  double dot = 0.0, ww = 0.0, oo = 0.0;
   for (int i = threadIdx.x; i < g.red_tiles; i += 256) {
     dot += part[3 * i + 0];
     ww += part[3 * i + 1];
@@ -564,26 +567,27 @@ __global__ __launch_bounds__(256) void tail_finalize_kernel(Batch bt, Work wk, i
   }
   block_sum3_256(dot, ww, oo, red);
   if (threadIdx.x == 0) {
-    const float coef = (variant == MUON_VARIANT_MUONGS && ww > 0.f) ? dot / ww : 0.f;
+    // totals in fp64; each scalar rounded to fp32 once
+    const double coef = (variant == MUON_VARIANT_MUONGS && ww > 0.0) ? dot / ww : 0.0;
     float hscale = 1.f;
     if (variant == MUON_VARIANT_MUONH) {
       // ||W^||^2 = ||d W - step O||^2 = d^2 ||W||^2 - 2 d step <W,O> + step^2 ||O||^2
       const double d = g.decay, st = g.step;
-      const double h2 = d * d * double(ww) - 2.0 * d * st * double(dot) + st * st * double(oo);
-      if (h2 > 0.0) hscale = float(sqrt(double(ww) / h2));
+      const double h2 = d * d * ww - 2.0 * d * st * dot + st * st * oo;
+      if (h2 > 0.0) hscale = float(sqrt(ww / h2));
     }
     float* sc = g.scal + tr.m * kScal;
-    sc[SC_R2] = ww;
-    sc[SC_DOT] = dot;
-    sc[SC_O2] = oo;
-    sc[SC_COEF] = coef;
+    sc[SC_R2] = float(ww);
+    sc[SC_DOT] = float(dot);
+    sc[SC_O2] = float(oo);
+    sc[SC_COEF] = float(coef);
     sc[SC_HSCALE] = hscale;
     if (g.stats) {
       float* st = g.stats + tr.m * MUON_STATS_PER_MATRIX;
-      st[1] = ww;
-      st[2] = dot;
-      st[3] = oo;
-      st[4] = fmaxf(oo - 2.f * coef * dot + coef * coef * ww, 0.f);
+      st[1] = float(ww);
+      st[2] = float(dot);
+      st[3] = float(oo);
+      st[4] = float(fmax(oo - 2.0 * coef * dot + coef * coef * ww, 0.0));
     }
     if (rc) rc_merge(g, tr.m, variant);
   }

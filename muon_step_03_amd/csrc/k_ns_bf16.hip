@@ -1159,23 +1159,24 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void ns_bf16_kernel(
     }
   }
   if (fred) {
-    // the tile's three sums, in a fixed order: wave shuffles, then the
-    // waves' values through LDS
+    // the tile's three sums, in a fixed order and in fp64 beyond the lanes'
+    // own: wave shuffles, then the waves' values through LDS
+    double rd = red_dot, rw = red_ww, ro = red_oo;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-      red_dot += __shfl_xor(red_dot, off, 64);
-      red_ww += __shfl_xor(red_ww, off, 64);
-      red_oo += __shfl_xor(red_oo, off, 64);
+      rd += __shfl_xor(rd, off, 64);
+      rw += __shfl_xor(rw, off, 64);
+      ro += __shfl_xor(ro, off, 64);
     }
-    __shared__ float red_lds[3 * C::NW];
+    __shared__ double red_lds[3 * C::NW];
     if (lane == 0) {
-      red_lds[wave] = red_dot;
-      red_lds[C::NW + wave] = red_ww;
-      red_lds[2 * C::NW + wave] = red_oo;
+      red_lds[wave] = rd;
+      red_lds[C::NW + wave] = rw;
+      red_lds[2 * C::NW + wave] = ro;
     }
     block_barrier();
     if (t < 3) {
-      float sum = 0.f;
+      double sum = 0.0;
 #pragma unroll
       for (int w = 0; w < C::NW; ++w) sum += red_lds[t * C::NW + w];
       g.tail_part[(m * g.red_tiles + tile) * 3 + t] = sum;

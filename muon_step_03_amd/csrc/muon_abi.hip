@@ -82,7 +82,7 @@ Layout make_layout(int64_t count, int64_t rows, int64_t cols, int dtype) {
   size_t x, a, h, t, s;
   const size_t c = size_t(count);
   if (!mul_ok(c, size_t(L.p_pad * L.q_pad) * es, &x) || !mul_ok(c, size_t(L.p_pad * L.p_pad) * es, &a) ||
-      !mul_ok(c, size_t(L.head_tiles) * 8, &h) || !mul_ok(c, size_t(L.tail_tiles) * 12, &t) ||
+      !mul_ok(c, size_t(L.head_tiles) * 8, &h) || !mul_ok(c, size_t(L.tail_tiles) * 24, &t) ||
       !mul_ok(c, size_t(kScal) * 4, &s))
     return L;  // total stays 0
   size_t rc, rcs, rcst;
@@ -454,7 +454,7 @@ int run_groups(const muon_group* groups, int ngroups, int dtype, double lr, doub
       m.a_stride = L.p_pad * L.p_pad;
       m.head_part = reinterpret_cast<double*>(base);
       base += L.head_bytes;
-      m.tail_part = reinterpret_cast<float*>(base);
+      m.tail_part = reinterpret_cast<double*>(base);
       base += L.tail_bytes;
       m.scal = reinterpret_cast<float*>(base);
       base += L.scal_bytes;

@@ -13,7 +13,7 @@
 //   A, B    [count][p_pad][p_pad]   Gram matrix X X^T and polynomial a I + b A + c A A
 //                                   (bf16 path; b A + c A A on the fp32 path)
 //   head    [count][head_tiles]     per-tile partial sums of u^2 (fp64)
-//   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2
+//   tail    [count][tail_tiles][3]  per-tile partials of <W,O>, ||W||^2, ||O||^2 (fp64)
 //                                   (red_tiles <= tail_tiles of them are used)
 //   scal    [count][kScal]          per-matrix scalars (norm, 1/(norm+eps), ...)
 //   rc      [count][tail_tiles][128] per-tile row and column sums of O^2
@@ -130,7 +130,7 @@ struct MatGroup {
   int64_t x_stride;    // elements between matrices in X0/X1
   int64_t a_stride;    // elements between matrices in A/B
   double* head_part;   // [count][head_tiles]: per-tile sums of u^2 (fp64)
-  float* tail_part;
+  double* tail_part;   // [count][red_tiles][3]: per-tile <W,O>, ||W||^2, ||O||^2 (fp64)
   float* rc_part;      // [count][tail_tiles][128]: per-tile row and column sums of O^2
   float* rc_norm2;     // [count][rows + cols]: squared row, then column norms of O
   float* rc_stat;      // [count][rc_chunks(rows, cols)][5]: per-chunk norm statistics

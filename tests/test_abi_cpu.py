@@ -64,7 +64,7 @@ def ws_formula(count, rows, cols, dtype):
     tail = math.ceil(rows / 64) * math.ceil(cols / 64)
     chunks = math.ceil(rows / 256) + math.ceil(cols / 256)
     return (2 * al(count * pp * qp * es) + 2 * al(count * pp * pp * es) + al(count * head * 8)
-            + al(count * tail * 12) + al(count * 10 * 4) + al(count * tail * 128 * 4)
+            + al(count * tail * 24) + al(count * 10 * 4) + al(count * tail * 128 * 4)
             + al(count * (rows + cols) * 4) + al(count * chunks * 5 * 4) + 256)
 
 

@@ -50,8 +50,9 @@
  *           group): ||U||_F, ||W||_F^2, <W,O>_F, ||O||_F^2, ||O~||_F^2 (the
  *           projected O for MuonGS, the equalised O for NorMuon/MeqMuon,
  *           ||O||^2 otherwise), of W and O before the update, returned as
- *           float32: each GPU thread sums its elements in float32 (float64
- *           for ||U||), and those partial sums are added in float64.
+ *           float32: the per-thread partial sums (float32 where the last
+ *           Newton-Schulz launch forms them, float64 elsewhere) are added
+ *           in float64.
  *           NULL skips them.
  *  Stream   a hipStream_t passed as void*; NULL is the default stream.  The
  *           call only enqueues work: it does not synchronise, allocate device
